@@ -1,0 +1,18 @@
+"""CPU fp64 oracle for exact attention. TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The GPU library never does, and this package never
+imports the GPU library.
+"""
+from .attention import (  # noqa: F401
+    attention_backward,
+    attention_forward,
+    bf16_bits_to_f64,
+    causal_visible,
+    exact_scale,
+    head_backward,
+    head_forward,
+    head_probs,
+    online_softmax_stats,
+    rows_forward,
+)

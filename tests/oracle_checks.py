@@ -1,0 +1,340 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each check takes the oracle module as an argument, so the same battery runs
+against the real oracle (every check must pass) and against copies of it with a
+planted mistake (at least one check must fail). None of them retypes the
+oracle's formulas: they use closed forms, invariants, finite differences, a
+scalar brute force written with math.fsum, and torch's CPU float64 softmax and
+autograd as an independent library routine.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+RTOL_EXACT = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(rng, *shape, sigma=1.0):
+    return rng.standard_normal(shape) * sigma
+
+
+def _max_rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(float(np.max(np.abs(b))), 1e-300)
+    return float(np.max(np.abs(a - b))) / den
+
+
+# --- C1: identical keys -------------------------------------------------------
+def check_identical_keys(orc):
+    rng = _rng(11)
+    for causal in (False, True):
+        n, d, scale = 9, 4, 0.37
+        q = _rand(rng, 1, 1, n, d)
+        krow = _rand(rng, d)
+        k = np.broadcast_to(krow, (1, 1, n, d)).copy()
+        v = _rand(rng, 1, 1, n, d)
+        o, lse = orc.attention_forward(q, k, v, causal, scale)
+        sc = float(np.float32(scale))
+        for i in range(n):
+            vis = (i + 1) if causal else n
+            assert np.allclose(o[0, 0, i], v[0, 0, :vis].mean(axis=0), rtol=0, atol=1e-12)
+            want = sc * float(q[0, 0, i] @ krow) + math.log(vis)
+            assert abs(lse[0, 0, i] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+# --- C2: N = 1 ----------------------------------------------------------------
+def check_single_token(orc):
+    rng = _rng(12)
+    for causal in (False, True):
+        q, k, v, do = (_rand(rng, 2, 3, 1, 5) for _ in range(4))
+        o, lse = orc.attention_forward(q, k, v, causal, 0.5)
+        assert np.array_equal(o, v)
+        assert np.allclose(lse, 0.5 * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-14)
+        dq, dk, dv = orc.attention_backward(q, k, v, do, causal, 0.5)
+        assert np.all(np.abs(dq) <= 1e-15) and np.all(np.abs(dk) <= 1e-15)
+        assert np.allclose(dv, do, rtol=0, atol=1e-15)
+
+
+# --- C3: causal row 0 -------------------------------------------------------
+def check_causal_row0(orc):
+    rng = _rng(13)
+    q, k, v, do = (_rand(rng, 1, 2, 7, 3) for _ in range(4))
+    o, lse = orc.attention_forward(q, k, v, True, 0.8)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+    sc = float(np.float32(0.8))
+    assert np.allclose(lse[:, :, 0], sc * np.sum(q[:, :, 0] * k[:, :, 0], axis=-1),
+                       rtol=0, atol=1e-14)
+    dq, _, _ = orc.attention_backward(q, k, v, do, True, 0.8)
+    assert np.all(np.abs(dq[:, :, 0]) <= 1e-15)
+
+
+# --- C4: softmax rows are a probability distribution -------------------------
+def check_prob_rows(orc):
+    rng = _rng(14)
+    for causal in (False, True):
+        q, k = _rand(rng, 33, 8, sigma=3.0), _rand(rng, 33, 8, sigma=3.0)
+        p, lse = orc.head_probs(q, k, causal, 0.3)
+        assert np.all(np.abs(p.sum(axis=1) - 1.0) <= 1e-12)
+        assert np.all(p >= 0)
+        if causal:
+            assert np.all(p[np.triu_indices(33, 1)] == 0.0)
+            assert np.all(p[np.tril_indices(33)] > 0.0)
+        # P_ij = exp(scale * q_i.k_j - LSE_i): the log-sum-exp normalises the row
+        sc = float(np.float32(0.3))
+        s = sc * (q @ k.T)
+        mask = np.tril(np.ones((33, 33), bool)) if causal else np.ones((33, 33), bool)
+        assert np.allclose(p[mask], np.exp(s - lse[:, None])[mask], rtol=1e-12, atol=0)
+
+
+# --- C5: constant V -----------------------------------------------------------
+def check_constant_v(orc):
+    rng = _rng(15)
+    for causal in (False, True):
+        q, k = _rand(rng, 1, 2, 10, 4), _rand(rng, 1, 2, 10, 4)
+        c = _rand(rng, 4)
+        v = np.broadcast_to(c, (1, 2, 10, 4)).copy()
+        do = _rand(rng, 1, 2, 10, 4)
+        o, _ = orc.attention_forward(q, k, v, causal, 0.6)
+        assert np.allclose(o, np.broadcast_to(c, o.shape), rtol=0, atol=1e-13)
+        dq, dk, _ = orc.attention_backward(q, k, v, do, causal, 0.6)
+        assert np.max(np.abs(dq)) <= 1e-13 and np.max(np.abs(dk)) <= 1e-13
+
+
+# --- C6: permutation equivariance (non-causal) -------------------------------
+def check_equivariance(orc):
+    rng = _rng(16)
+    q, k, v = (_rand(rng, 1, 1, 12, 5) for _ in range(3))
+    o, lse = orc.attention_forward(q, k, v, False, 0.45)
+    pk = rng.permutation(12)
+    o2, lse2 = orc.attention_forward(q, k[:, :, pk], v[:, :, pk], False, 0.45)
+    assert np.allclose(o2, o, rtol=0, atol=1e-13) and np.allclose(lse2, lse, rtol=0, atol=1e-13)
+    pq = rng.permutation(12)
+    o3, lse3 = orc.attention_forward(q[:, :, pq], k, v, False, 0.45)
+    assert np.allclose(o3, o[:, :, pq], rtol=0, atol=1e-13)
+    assert np.allclose(lse3, lse[:, :, pq], rtol=0, atol=1e-13)
+
+
+# --- C7: shift invariance of the keys ----------------------------------------
+def check_key_shift(orc):
+    rng = _rng(17)
+    for causal in (False, True):
+        q, k, v = (_rand(rng, 1, 1, 11, 6) for _ in range(3))
+        u = _rand(rng, 6)
+        o, lse = orc.attention_forward(q, k, v, causal, 0.7)
+        o2, lse2 = orc.attention_forward(q, k + u, v, causal, 0.7)
+        sc = float(np.float32(0.7))
+        assert np.allclose(o2, o, rtol=0, atol=1e-12)
+        assert np.allclose(lse2, lse + sc * (q[0, 0] @ u)[None, None, :], rtol=0, atol=1e-12)
+
+
+# --- C8: backward identities --------------------------------------------------
+def backward_identities(q, k, v, o, do, dq, dk, dv, scale, causal):
+    """Residuals of identities every exact attention backward satisfies, per head.
+
+    Returns a dict of max-normalised residuals:
+      sum_j dK_j = 0; sum_j dV_j = sum_i dO_i; <dQ,Q> = <dK,K>.
+    (The first holds because each softmax row's dS sums to zero.)
+    """
+    res = {}
+    dk_sum = dk.sum(axis=-2)
+    res["sum_dk"] = float(np.max(np.abs(dk_sum))) / max(float(np.max(np.abs(dk))), 1e-300)
+    dv_sum, do_sum = dv.sum(axis=-2), do.sum(axis=-2)
+    res["sum_dv"] = float(np.max(np.abs(dv_sum - do_sum))) / max(float(np.max(np.abs(do_sum))), 1e-300)
+    a = np.einsum("bhnd,bhnd->bh", dq, q)
+    b = np.einsum("bhnd,bhnd->bh", dk, k)
+    scale_ab = np.maximum(np.einsum("bhnd,bhnd->bh", np.abs(dq), np.abs(q)),
+                          np.einsum("bhnd,bhnd->bh", np.abs(dk), np.abs(k)))
+    res["qdq_kdk"] = float(np.max(np.abs(a - b) / np.maximum(scale_ab, 1e-300)))
+    return res
+
+
+def check_backward_identities(orc):
+    rng = _rng(18)
+    for causal in (False, True):
+        q, k, v, do = (_rand(rng, 2, 2, 13, 5) for _ in range(4))
+        o, _ = orc.attention_forward(q, k, v, causal, 0.55)
+        dq, dk, dv = orc.attention_backward(q, k, v, do, causal, 0.55)
+        res = backward_identities(q, k, v, o, do, dq, dk, dv, 0.55, causal)
+        assert all(r <= 1e-10 for r in res.values()), res
+        # and D_i = dO_i . O_i equals sum_j P_ij dP_ij
+        for b in range(2):
+            for h in range(2):
+                p, _ = orc.head_probs(q[b, h], k[b, h], causal, 0.55)
+                dp = do[b, h] @ v[b, h].T
+                assert np.allclose((p * dp).sum(1), (do[b, h] * o[b, h]).sum(1), rtol=1e-10, atol=1e-12)
+
+
+# --- C9: finite differences ---------------------------------------------------
+def check_finite_differences(orc):
+    rng = _rng(19)
+    h = 1e-6
+    for n in (1, 2, 3, 5, 8):
+        for d in (1, 2, 4):
+            for causal in (False, True):
+                q, k, v, do = (_rand(rng, 1, 2, n, d) for _ in range(4))
+                scale = 0.9
+
+                def loss(q_, k_, v_):
+                    o_, _ = orc.attention_forward(q_, k_, v_, causal, scale)
+                    return float(np.sum(o_ * do))
+
+                grads = orc.attention_backward(q, k, v, do, causal, scale)
+                for which, g in enumerate(grads):
+                    fd = np.zeros_like(g)
+                    args = [q, k, v]
+                    for idx in np.ndindex(*g.shape):
+                        plus = [a.copy() for a in args]
+                        minus = [a.copy() for a in args]
+                        plus[which][idx] += h
+                        minus[which][idx] -= h
+                        fd[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+                    den = max(float(np.max(np.abs(fd))), 1.0)
+                    err = float(np.max(np.abs(fd - g))) / den
+                    assert err <= 1e-6, (n, d, causal, which, err)
+
+
+# --- C10: scalar brute force (pure Python) -------------------------------------
+def brute_force(q, k, v, do, causal, scale):
+    """Attention and its gradient with loops, math.exp and math.fsum only.
+
+    The gradient here goes through the softmax Jacobian written out per entry:
+    dL/dS_ij = P_ij * (dO_i . v_j - dO_i . O_i).
+    """
+    sc = float(np.float32(scale))
+    n, d = len(q), len(q[0])
+    o = [[0.0] * d for _ in range(n)]
+    lse = [0.0] * n
+    probs = [[0.0] * n for _ in range(n)]
+    for i in range(n):
+        keys = range(i + 1) if causal else range(n)
+        s = {j: sc * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in keys}
+        m = max(s.values())
+        e = {j: math.exp(s[j] - m) for j in keys}
+        tot = math.fsum(e.values())
+        lse[i] = m + math.log(tot)
+        for j in keys:
+            probs[i][j] = e[j] / tot
+        for c in range(d):
+            o[i][c] = math.fsum(probs[i][j] * v[j][c] for j in keys)
+    dq = [[0.0] * d for _ in range(n)]
+    dk = [[0.0] * d for _ in range(n)]
+    dv = [[0.0] * d for _ in range(n)]
+    for i in range(n):
+        do_o = math.fsum(do[i][c] * o[i][c] for c in range(d))
+        for j in range(n):
+            pij = probs[i][j]
+            if pij == 0.0:
+                continue
+            do_v = math.fsum(do[i][c] * v[j][c] for c in range(d))
+            g = pij * (do_v - do_o)
+            for c in range(d):
+                dq[i][c] += sc * g * k[j][c]
+                dk[j][c] += sc * g * q[i][c]
+                dv[j][c] += pij * do[i][c]
+    return o, lse, dq, dk, dv
+
+
+def check_brute_force(orc):
+    rng = _rng(20)
+    for n in (1, 2, 4, 6):
+        for d in (1, 3, 4):
+            for causal in (False, True):
+                q, k, v, do = (_rand(rng, 1, 1, n, d, sigma=1.5) for _ in range(4))
+                o, lse = orc.attention_forward(q, k, v, causal, 0.65)
+                dq, dk, dv = orc.attention_backward(q, k, v, do, causal, 0.65)
+                bo, blse, bdq, bdk, bdv = brute_force(q[0, 0].tolist(), k[0, 0].tolist(),
+                                                      v[0, 0].tolist(), do[0, 0].tolist(),
+                                                      causal, 0.65)
+                for mine, ref in ((o[0, 0], bo), (lse[0, 0], blse), (dq[0, 0], bdq),
+                                  (dk[0, 0], bdk), (dv[0, 0], bdv)):
+                    ref = np.asarray(ref)
+                    assert np.max(np.abs(mine - ref)) <= 1e-12 * max(1.0, float(np.max(np.abs(ref))))
+
+
+# --- C11: torch CPU float64 softmax + autograd ---------------------------------
+def check_torch_cross(orc):
+    import torch
+    rng = _rng(21)
+    for causal in (False, True):
+        for n, d in ((1, 8), (17, 8), (64, 16)):
+            q, k, v, do = (_rand(rng, 2, 2, n, d) for _ in range(4))
+            scale = float(np.float32(1.0 / math.sqrt(d)))
+            tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+            s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+            if causal:
+                mask = torch.ones(n, n, dtype=torch.bool).triu(1)
+                s = s.masked_fill(mask, float("-inf"))
+            to = torch.matmul(torch.softmax(s, dim=-1), tv)
+            tlse = torch.logsumexp(s, dim=-1)
+            (to * torch.tensor(do)).sum().backward()
+            o, lse = orc.attention_forward(q, k, v, causal, scale)
+            dq, dk, dv = orc.attention_backward(q, k, v, do, causal, scale)
+            for mine, ref in ((o, to.detach().numpy()), (lse, tlse.detach().numpy()),
+                              (dq, tq.grad.numpy()), (dk, tk.grad.numpy()), (dv, tv.grad.numpy())):
+                assert _max_rel(mine, ref) <= 1e-12, (causal, n, d)
+
+
+# --- C12: the page's tile recurrence reproduces the two-pass statistics -----
+def check_online_recurrence(orc):
+    rng = _rng(22)
+    for trial in range(50):
+        n = int(rng.integers(1, 300))
+        x = rng.standard_normal(n) * float(rng.choice([0.1, 1.0, 9.0, 40.0]))
+        cuts = np.sort(rng.choice(np.arange(1, n), size=min(n - 1, int(rng.integers(0, 8))),
+                                  replace=False)) if n > 1 else np.array([], int)
+        edges = [0, *cuts.tolist(), n]
+        tiles = [(edges[t], edges[t + 1]) for t in range(len(edges) - 1)]
+        order = rng.permutation(len(tiles))
+        m, l = orc.online_softmax_stats(x, [tiles[t] for t in order])
+        m_ref = float(x.max())
+        l_ref = math.fsum(math.exp(float(t) - m_ref) for t in x)
+        assert m == m_ref
+        assert abs(l - l_ref) <= 1e-12 * l_ref
+
+
+# --- bf16 decode --------------------------------------------------------------
+def check_bf16_decode(orc):
+    import torch
+    rng = _rng(23)
+    bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    mine = orc.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+
+
+# --- rows_forward agrees with the full forward ---------------------------------
+def check_rows_forward(orc):
+    rng = _rng(24)
+    for causal in (False, True):
+        q, k, v = (_rand(rng, 1, 1, 40, 6) for _ in range(3))
+        o, lse = orc.attention_forward(q, k, v, causal, 0.4)
+        rows = np.array([0, 1, 7, 39])
+        ro, rl = orc.rows_forward(q[0, 0, rows], k[0, 0], v[0, 0], rows, causal, 0.4)
+        assert np.allclose(ro, o[0, 0, rows], rtol=0, atol=1e-13)
+        assert np.allclose(rl, lse[0, 0, rows], rtol=0, atol=1e-13)
+
+
+ALL_CHECKS = [
+    check_identical_keys,
+    check_single_token,
+    check_causal_row0,
+    check_prob_rows,
+    check_constant_v,
+    check_equivariance,
+    check_key_shift,
+    check_backward_identities,
+    check_finite_differences,
+    check_brute_force,
+    check_torch_cross,
+    check_online_recurrence,
+    check_bf16_decode,
+    check_rows_forward,
+]

@@ -1,0 +1,79 @@
+"""Each plausible mistake planted in a copy of the oracle fails some pin.
+
+The oracle's source is copied, one edit is applied to the copy (a dropped
+term, a wrong sign, a wrong index or axis, a transposed operand), the copy is
+loaded as a separate module on the CPU, and the full pin battery must reject it.
+The real oracle is never modified.
+"""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from tests import oracle_checks as oc
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "attention.py")
+
+MUTANTS = {
+    "dropped_scale": ("s = sc * (q @ k.T)", "s = (q @ k.T)"),
+    "mask_direction": ("return np.tril(np.ones((n, n), dtype=bool))",
+                       "return np.triu(np.ones((n, n), dtype=bool))"),
+    "mask_strict": ("return np.tril(np.ones((n, n), dtype=bool))",
+                    "return np.tril(np.ones((n, n), dtype=bool), -1) | (np.arange(n) == 0)[None, :]"),
+    "lse_dropped_max": ("lse = m[:, 0] + np.log(l[:, 0])", "lse = np.log(l[:, 0])"),
+    "lse_log2": ("lse = m[:, 0] + np.log(l[:, 0])", "lse = m[:, 0] + np.log2(l[:, 0])"),
+    "sum_wrong_axis": ("l = e.sum(axis=1, keepdims=True)\n    p = e / l",
+                       "l = e.sum(axis=0, keepdims=True)\n    p = e / l"),
+    "pv_transposed": ("return p @ v, lse", "return p.T @ v, lse"),
+    "dv_untransposed": ("dv = p.T @ do", "dv = p @ do"),
+    "dp_transposed": ("dp = do @ v.T", "dp = (do @ v.T).T"),
+    "ds_sign": ("ds = p * (dp - dvec)", "ds = p * (dp + dvec)"),
+    "ds_dropped_d": ("ds = p * (dp - dvec)", "ds = p * dp"),
+    "d_wrong_axis": ("dvec = (p * dp).sum(axis=1, keepdims=True)",
+                     "dvec = (p * dp).sum(axis=0, keepdims=True)"),
+    "dq_transposed": ("dq = sc * (ds @ k)", "dq = sc * (ds.T @ k)"),
+    "dk_untransposed": ("dk = sc * (ds.T @ q)", "dk = sc * (ds @ q)"),
+    "dk_dropped_scale": ("dk = sc * (ds.T @ q)", "dk = (ds.T @ q)"),
+    "rows_mask_strict": ("s = np.where(j <= np.asarray(rows)[:, None], s, -np.inf)",
+                         "s = np.where(j < np.asarray(rows)[:, None] + (j == 0), s, -np.inf)"),
+    "recurrence_no_rescale": ("l = l * alpha + float(np.exp(t - m_new).sum())",
+                              "l = l + float(np.exp(t - m_new).sum())"),
+    "recurrence_alpha_sign": ("alpha = 0.0 if m == -np.inf else np.exp(m - m_new)",
+                              "alpha = 0.0 if m == -np.inf else np.exp(m_new - m)"),
+    "decode_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+}
+
+
+def _load_mutant(name, old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation {name} does not match the oracle source exactly once"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(text.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def _battery_fails(mod):
+    for check in oc.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:
+            return check.__name__
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    mod = _load_mutant(name, old, new)
+    caught_by = _battery_fails(mod)
+    assert caught_by is not None, f"planted mistake {name!r} passed every pin"
+
+
+def test_unmutated_copy_passes():
+    spec = importlib.util.spec_from_file_location("oracle_copy", SRC)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert _battery_fails(mod) is None
