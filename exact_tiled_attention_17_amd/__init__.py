@@ -1,0 +1,161 @@
+"""Exact tiled attention for AMD Instinct MI355X (gfx950).
+
+A thin binding of ``libfa.so`` (C ABI in ``include/fa.h``). The functions
+``fa_fwd``, ``fa_bwd`` and ``fa_status_string`` mirror the C entry points one
+to one (raw device pointers as Python ints, ``stream`` as a hipStream_t
+handle). ``forward`` and ``backward`` are conveniences over torch tensors:
+they check dtypes and shapes, allocate outputs with torch and pass
+``data_ptr()`` and the current stream; every step of the computation runs in
+the library's HIP kernels. There is no fallback: if the library is missing
+or cannot be loaded, every call raises.
+
+Tensor layout is [batch, heads, seq_len, head_dim] as on "RTX Flash Attention
+Implementation COMPLETE" (Usage Examples), bf16, contiguous; the LSE is
+float32 [batch, heads, seq_len].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_status_string", "fa_last_hip_error", "forward", "backward", "load",
+           "FAError", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+FA_ERR_OUT_OF_MEMORY = 4
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {fa_status_string(status)}"
+        if status in (FA_ERR_HIP, FA_ERR_OUT_OF_MEMORY):
+            msg += f" ({fa_last_hip_error()})"
+        super().__init__(msg)
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Loads libfa.so once and declares its exported signatures.
+
+    torch is imported first: torch ships its own HIP runtime under the same
+    soname as the system one, and libfa.so must bind to the runtime instance
+    that owns the caller's device memory and streams (a second runtime in the
+    same process sees no device).
+    """
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (binds libamdhip64 to torch's runtime)
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing; build it with `python -m exact_tiled_attention_17_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+    lib.fa_fwd.restype = ci
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+    lib.fa_bwd.restype = ci
+    lib.fa_status_string.argtypes = [ci]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_last_hip_error() -> str:
+    return load().fa_last_hip_error().decode()
+
+
+def fa_fwd(Q, K, V, O, LSE, B, H, N, d, causal, softmax_scale, stream) -> int:
+    """C ``fa_fwd``: pointers as ints (LSE may be 0 / None); returns the status."""
+    return load().fa_fwd(Q, K, V, O, LSE or None, B, H, N, d, int(causal),
+                         float(softmax_scale), stream or None)
+
+
+def fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal, softmax_scale, stream) -> int:
+    """C ``fa_bwd``: pointers as ints; returns the status."""
+    return load().fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, int(causal),
+                         float(softmax_scale), stream or None)
+
+
+def _check(name, t, shape, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, *, out=None, lse=None,
+            need_lse: bool = True):
+    """O, LSE = attention(q, k, v). q, k, v: bf16 [B, H, N, d] on one GPU."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, seq_len, head_dim]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, N, d), torch.bfloat16, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("out", out, (B, H, N, d), torch.bfloat16, dev)
+    if need_lse:
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        _check("lse", lse, (B, H, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                    lse.data_ptr() if need_lse else None, B, H, N, d, causal,
+                    _scale(scale, d), stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def backward(do, q, k, v, o, lse, causal: bool = False, scale: float | None = None, *,
+             dq=None, dk=None, dv=None):
+    """dQ, dK, dV of attention given dO, the inputs, and the forward's O and LSE."""
+    import torch
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("do", do), ("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(name, t, (B, H, N, d), torch.bfloat16, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), torch.bfloat16, dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    B, H, N, d, causal, _scale(scale, d), stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

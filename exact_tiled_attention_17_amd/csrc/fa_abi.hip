@@ -1,0 +1,96 @@
+// C ABI of the exact tiled attention library (declared in include/fa.h).
+// Validation is pure host code and happens before any HIP call; a call that
+// fails validation enqueues nothing.
+
+#include <stdint.h>
+
+#include <cmath>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e, int status_on_error) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = e;
+  return status_on_error;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int B, int H, int N, int d, int causal, float scale) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)N * d >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  // grid sizes: at most ceil(N/32) workgroups per head, one head per (b, h)
+  const long long tiles = ((long long)N + 31) / 32;
+  if ((long long)B * H > (1LL << 31) / tiles) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int check_tensor(const void* p) {
+  if (p == nullptr || !aligned(p, 16)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+           int d, int causal, float softmax_scale, void* stream) {
+  int st = check_common(B, H, N, d, causal, softmax_scale);
+  if (st != FA_OK) return st;
+  for (const void* p : {Q, K, V, (const void*)O})
+    if ((st = check_tensor(p)) != FA_OK) return st;
+  if (LSE != nullptr && !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a{Q, K, V, O, LSE, B, H, N, d, causal != 0, softmax_scale,
+                reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_fwd(a), FA_ERR_HIP);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+           const void* dO, void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal,
+           float softmax_scale, void* stream) {
+  int st = check_common(B, H, N, d, causal, softmax_scale);
+  if (st != FA_OK) return st;
+  for (const void* p : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
+    if ((st = check_tensor(p)) != FA_OK) return st;
+  if (LSE == nullptr || !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t rows = (size_t)B * H * N;
+  void* scratch = nullptr;
+  const hipError_t m = hipMallocAsync(&scratch, fa::bwd_scratch_bytes(B, H, N, d), s);
+  if (m != hipSuccess || scratch == nullptr)
+    return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
+  float* dq_acc = static_cast<float*>(scratch);
+  float* rowstat = dq_acc + rows * (size_t)d;
+  fa::BwdArgs a{Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal != 0, softmax_scale, s,
+                dq_acc, rowstat};
+  const hipError_t e = fa::launch_bwd(a);
+  const hipError_t f = hipFreeAsync(scratch, s);
+  return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG: null or misaligned pointer, bad shape, scale or causal flag";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call or kernel launch failed";
+    case FA_ERR_OUT_OF_MEMORY: return "FA_ERR_OUT_OF_MEMORY: backward scratch allocation failed";
+    default: return "unknown fa_status";
+  }
+}
+
+const char* fa_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// vector types for bf16 MFMA operands, 128-bit memory moves, cross-lane
+// reductions within a 64-wide wavefront, and the launch plumbing that maps
+// workgroups onto the eight XCDs of an MI355X.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// One 32x32x16 bf16 matrix-core product with float32 accumulation.
+// Operand layout for a 64-lane wave (lane l, half h = l / 32):
+//   A (32 x 16): lane l holds row l % 32, k = 8h .. 8h+7
+//   B (16 x 32): lane l holds column l % 32, k = 8h .. 8h+7
+//   C (32 x 32): lane l holds column l % 32, rows 8*(r/4) + 4h + r%4, r = 0..15
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Lanes l and l ^ 32 exchange values; returns (own, partner) in some order,
+// so symmetric reductions (max, sum) over the pair are exact either way.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// float32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_global8(void* p, u32x2 v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+__device__ __forceinline__ bf16x8 ld_lds16(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void st_lds16(__bf16* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ void st_lds8(__bf16* p, u32x2 v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+
+// Interleave four rows of eight bf16 (one 16-byte chunk each, rows r0..r3)
+// into eight 4-element columns: column e = (r0[e], r1[e], r2[e], r3[e]).
+// Used to write a transposed tile into LDS with 8-byte stores.
+__device__ __forceinline__ void transpose4x8(const u32x4& r0, const u32x4& r1, const u32x4& r2,
+                                             const u32x4& r3, u32x2 col[8]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t a = r0[m], b = r1[m], c = r2[m], d = r3[m];
+    // even element (low halves) and odd element (high halves) of dword m
+    col[2 * m][0] = (a & 0xFFFFu) | (b << 16);
+    col[2 * m][1] = (c & 0xFFFFu) | (d << 16);
+    col[2 * m + 1][0] = (a >> 16) | (b & 0xFFFF0000u);
+    col[2 * m + 1][1] = (c >> 16) | (d & 0xFFFF0000u);
+  }
+}
+
+// Position of item x (0..15 within each group of 16) in a transposed operand
+// tile: bits 2 and 3 swap. With the MFMA C layout above, a lane's 8 values for
+// one 16-wide k step are items {4h..4h+3, 8+4h..8+4h+3}; after this swap they
+// sit at positions 8h..8h+7, so a B/A-operand read is one 16-byte load.
+__device__ __forceinline__ int kperm(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Maps a linear workgroup id to (head, tile) so that the workgroups that land
+// on one XCD (the hardware deals ids round-robin over the 8 XCDs) cover whole
+// heads, which then share that XCD's L2; within an XCD, heads go one after the
+// other and each head's tiles go in the order `tile_of` gives.
+__device__ __forceinline__ void xcd_remap(int bid, int total, int tiles, int& head, int& tile) {
+  int v = bid;
+  if (total % kXcds == 0) {
+    const int per = total / kXcds;
+    v = (bid % kXcds) * per + bid / kXcds;
+  }
+  head = v / tiles;
+  tile = v % tiles;
+}
+
+}  // namespace fa

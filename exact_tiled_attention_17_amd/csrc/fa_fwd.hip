@@ -1,0 +1,265 @@
+// Forward pass of exact tiled attention on gfx950.
+//
+// The method is the tiled attention with an online softmax of "RTX Flash
+// Attention Implementation COMPLETE" (Technical Implementation Details: the
+// running max m and running sum l, and the Q-block / KV-block tiling), with the
+// causal masking of that page's Advanced Features. What this kernel does on
+// MI355X:
+//
+//  * One workgroup owns BR = 32 * NW query rows of one (batch, head); each of
+//    its NW waves owns 32 of them for the whole sweep over the keys.
+//  * Both products are computed transposed, S^T = K Q^T and O^T = V^T P^T,
+//    on 32x32x16 bf16 matrix cores. In the accumulator layout of S^T every lane
+//    then holds 16 scores of a single query row (its partner lane l ^ 32 holds
+//    the other 16), so the row max needs one cross-lane swap, the row sum none
+//    until the end, and the rescale factor of a lane's O^T accumulators is the
+//    lane's own. P^T goes from the S^T registers straight into the B operand of
+//    the second product (no LDS round trip); V^T is stored with its keys
+//    permuted to match.
+//  * K/V tiles of BC = 64 keys are staged in LDS, double buffered: the global
+//    loads of tile j+1 are issued before tile j is computed and written to LDS
+//    after it, one barrier per tile. K is kept row-major with an XOR swizzle on
+//    16-byte chunks (conflict-free operand reads); V is written transposed.
+//  * Causal: tiles entirely above the diagonal are never loaded; a wave skips
+//    tiles fully masked for its own rows; masks are applied only to tiles that
+//    cross the diagonal or the end of the sequence.
+//  * The softmax runs in base 2 in float32: c = scale * log2(e) is folded into
+//    one FMA per score; P is rounded to bf16 for the matrix core and the row
+//    sum l is accumulated from those same rounded values (dot2 with 1s).
+
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D, int NW>
+struct FwdCfg {
+  static constexpr int BR = 32 * NW;  // query rows per workgroup
+  static constexpr int BC = 64;       // keys per K/V tile
+  static constexpr int CH = D / 8;    // 16-byte chunks per row
+  static constexpr int VTS = BC + 8;  // padded row length (elements) of the V^T tile
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int LOADERS = THREADS / 2;  // half the threads load K, half V
+  static constexpr int KPT = BC * CH / LOADERS;        // K chunks per loader thread
+  static constexpr int VPT = (BC / 4) * CH / LOADERS;  // V 4-key groups per loader thread
+  static_assert(KPT >= 1 && VPT >= 1 && KPT == 4 * VPT, "loader split");
+  static_assert(BC * CH % LOADERS == 0 && (BC / 4) * CH % LOADERS == 0, "loader split");
+};
+
+template <int D, int NW, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW)))
+void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                float* __restrict__ LSE, int N, int BH, float c_log2) {
+  using C = FwdCfg<D, NW>;
+  constexpr int BR = C::BR, BC = C::BC, CH = C::CH, VTS = C::VTS;
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vt[2][D * VTS];
+
+  const int nq = (N + BR - 1) / BR;
+  int bh, qt;
+  xcd_remap(blockIdx.x, nq * BH, nq, bh, qt);
+  if (CAUSAL) qt = nq - 1 - qt;  // longest rows first
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const __bf16* Qh = Q + head;
+  const __bf16* Kh = K + head;
+  const __bf16* Vh = V + head;
+
+  const int q0 = qt * BR;
+  const int wrow0 = q0 + 32 * wave;  // first query row of this wave
+  const int row = wrow0 + l32;       // this lane's query row
+  const int nkv_all = (N + BC - 1) / BC;
+  const int last_row_wg = min(q0 + BR, N) - 1;
+  const int nkv = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;
+  const bool wave_active = wrow0 < N;
+  const int jw_last = CAUSAL ? min(wrow0 + 31, N - 1) / BC : nkv - 1;
+
+  // ---- Q^T operand: lane holds row `row`, d = 16 s + 8 hh .. +7 -------------
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < N) v = ld_global16(Qh + (size_t)row * D + 16 * s + 8 * hh);
+    qf[s] = as_bf16x8(v);
+  }
+
+  // ---- K/V tile staging -----------------------------------------------------
+  const bool k_loader = tid < C::LOADERS;
+  const int lt = k_loader ? tid : tid - C::LOADERS;
+  u32x4 stg[C::KPT];
+
+  auto load_tile = [&](int j) {
+    const int kv0 = j * BC;
+    if (k_loader) {
+#pragma unroll
+      for (int r = 0; r < C::KPT; ++r) {
+        const int i = lt + r * C::LOADERS;
+        const int key = i / CH, c = i % CH;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (kv0 + key < N) v = ld_global16(Kh + (size_t)(kv0 + key) * D + 8 * c);
+        stg[r] = v;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < C::VPT; ++r) {
+        const int g = lt + r * C::LOADERS;
+        const int kg = g / CH, dc = g % CH;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 4 * kg + i;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (kv0 + key < N) v = ld_global16(Vh + (size_t)(kv0 + key) * D + 8 * dc);
+          stg[4 * r + i] = v;
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if (k_loader) {
+#pragma unroll
+      for (int r = 0; r < C::KPT; ++r) {
+        const int i = lt + r * C::LOADERS;
+        const int key = i / CH, c = i % CH;
+        st_lds16(&ks[buf][key * D + ((c ^ (key & (CH - 1))) * 8)], stg[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < C::VPT; ++r) {
+        const int g = lt + r * C::LOADERS;
+        const int kg = g / CH, dc = g % CH;
+        u32x2 col[8];
+        transpose4x8(stg[4 * r], stg[4 * r + 1], stg[4 * r + 2], stg[4 * r + 3], col);
+        const int pos = kperm(4 * kg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st_lds8(&vt[buf][(8 * dc + e) * VTS + pos], col[e]);
+      }
+    }
+  };
+
+  // ---- running state ----------------------------------------------------------
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
+  float m_run = -INFINITY;  // running max of c * s over the row (base-2 units)
+  float l_run = 0.f;        // this lane's share of the running sum
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkv) load_tile(j + 1);
+
+    if (wave_active && j <= jw_last) {
+      // S^T = K_j Q^T : two 32-key blocks
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        s[kb] = f32x16{};
+        const int key = 32 * kb + l32;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          const int c = 2 * st + hh;
+          const bf16x8 a = ld_lds16(&ks[buf][key * D + ((c ^ (key & (CH - 1))) * 8)]);
+          s[kb] = mfma32(a, qf[st], s[kb]);
+        }
+      }
+      // masks: causal (key > row) and sequence end (key >= N), only where needed
+      const int kv0 = j * BC;
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= N || (CAUSAL && key > row)) s[kb][r] = -INFINITY;
+          }
+      }
+      // online softmax (base 2)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx * c_log2);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+
+      u32x4 pf[BC / 16];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e], c_log2, -m_new));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e + 1], c_log2, -m_new));
+            const uint32_t pk = pack_bf16(p0, p1);
+            pf[2 * kb + t][e] = pk;
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
+          }
+      l_run = l_run * alpha + lsum;
+
+      // O^T = alpha * O^T + V^T P^T
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        o[b] *= alpha;
+#pragma unroll
+        for (int t = 0; t < BC / 16; ++t) {
+          const bf16x8 a = ld_lds16(&vt[buf][(32 * b + l32) * VTS + 16 * t + 8 * hh]);
+          o[b] = mfma32(a, as_bf16x8(pf[t]), o[b]);
+        }
+      }
+    }
+
+    if (j + 1 < nkv) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l) ------------------------
+  if (!wave_active) return;
+  const float l_tot = pair_sum(l_run);
+  if (row >= N) return;
+  const float inv = 1.f / l_tot;
+  __bf16* Orow = O + head + (size_t)row * D;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16(o[b][4 * g] * inv, o[b][4 * g + 1] * inv);
+      w[1] = pack_bf16(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
+      st_global8(Orow + 32 * b + 8 * g + 4 * hh, w);
+    }
+  if (LSE != nullptr && hh == 0)
+    LSE[(size_t)bh * N + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+}
+
+template <int D, int NW, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a) {
+  using C = FwdCfg<D, NW>;
+  const int nq = (a.N + C::BR - 1) / C::BR;
+  const long long total = (long long)nq * a.B * a.H;
+  return launch_kernel(fwd_kernel<D, NW, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+                       (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
+                       a.LSE, a.N, a.B * a.H, a.softmax_scale * kLog2e);
+}
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_fwd_t<128, 8, true>(a) : launch_fwd_t<128, 8, false>(a);
+  return a.causal ? launch_fwd_t<64, 4, true>(a) : launch_fwd_t<64, 4, false>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,111 @@
+/*
+ * fa.h - exact tiled attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation is exact scaled-dot-product attention computed tile by tile
+ * with an online softmax, as described on "RTX Flash Attention Implementation
+ * COMPLETE" (Executive Summary; Technical Implementation Details, 1. Online
+ * Softmax Algorithm and 2. Memory Tiling Strategy; Usage Examples) and, for
+ * the backward that recomputes the probabilities from the stored log-sum-exp,
+ * "GPU Performance Optimization Batch 1 - Design Spec", Item 3 (Design).
+ *
+ * For one (batch b, head h), with q_i, k_j, v_j the rows of Q, K, V:
+ *   s_ij   = softmax_scale * q_i . k_j
+ *   vis(i) = { j : j <= i } if causal, else all j     (key j visible to query i)
+ *   LSE_i  = ln sum_{j in vis(i)} exp(s_ij)            (natural log)
+ *   P_ij   = exp(s_ij - LSE_i) for j in vis(i), else 0
+ *   O_i    = sum_j P_ij v_j
+ * and, given dO (the gradient of the loss with respect to O):
+ *   dV_j = sum_i P_ij dO_i
+ *   dS_ij = P_ij (dO_i . v_j - dO_i . O_i)
+ *   dQ_i = softmax_scale * sum_j dS_ij k_j,   dK_j = softmax_scale * sum_i dS_ij q_i
+ *
+ * Layout. Every tensor is dense and contiguous in row-major order:
+ *   Q, K, V, O, dO, dQ, dK, dV : [B, H, N, d] bfloat16 (raw 16-bit storage)
+ *   LSE                        : [B, H, N]    float32
+ * Pointers are device pointers on the current HIP device. bf16 tensors must be
+ * 16-byte aligned, LSE 4-byte aligned. Outputs are overwritten, never
+ * accumulated into; they must not alias the inputs.
+ *
+ * Limits: d in {64, 128}; N >= 1; B, H >= 1; N * d < 2^31 and
+ * B * H * ceil(N / 32) < 2^31; softmax_scale finite and > 0; causal in {0, 1}.
+ *
+ * Precision. Inputs are read as bf16; both contractions run on bf16 matrix
+ * cores with float32 accumulation; the softmax runs in float32. O, dQ, dK, dV
+ * are rounded to bf16 with round-to-nearest-even; LSE is float32.
+ *
+ * Errors and threading. Every entry point validates its arguments on the host
+ * before any HIP call and returns an fa_status. FA_ERR_HIP means a HIP call or
+ * kernel launch failed at enqueue time; faults inside a kernel surface at the
+ * caller's next synchronisation. Calls only enqueue work on `stream` (a
+ * hipStream_t; NULL is the default stream) and return; results are valid once
+ * the stream has reached them. The library holds no global mutable state (only
+ * a per-thread record of the last HIP error), so calls from several threads on
+ * different streams are safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad shape, bad scale or flag */
+  FA_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128 */
+  FA_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
+  FA_ERR_OUT_OF_MEMORY = 4  /* fa_bwd could not get its scratch memory */
+} fa_status;
+
+/*
+ * Forward pass ("RTX Flash Attention Implementation COMPLETE", Usage Examples:
+ * forward(q, k, v, causal, scale) returning the output and the LSE).
+ *
+ *   Q, K, V  in : [B,H,N,d] bf16
+ *   O        out: [B,H,N,d] bf16
+ *   LSE      out: [B,H,N] float32, natural-log log-sum-exp of the scaled,
+ *                 masked logits of each query row; may be NULL (not written).
+ *
+ * Allocates nothing. Returns FA_OK or an error status (nothing is enqueued on
+ * error).
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int H, int N, int d, int causal, float softmax_scale,
+           void* stream);
+
+/*
+ * Backward pass (same page, Usage Examples: backward(dout, q, k, v, out, lse,
+ * causal, scale) returning dq, dk, dv; "GPU Performance Optimization Batch 1 -
+ * Design Spec", Item 3, Design: the probabilities are recomputed from the
+ * stored LSE instead of keeping the N x N matrix).
+ *
+ *   Q, K, V, O, dO  in : [B,H,N,d] bf16 (O and LSE as produced by fa_fwd with
+ *                        the same causal flag and scale)
+ *   LSE             in : [B,H,N] float32, must not be NULL
+ *   dQ, dK, dV      out: [B,H,N,d] bf16
+ *
+ * Needs float32 scratch of 4*B*H*N*(d+2) bytes, taken stream-ordered with
+ * hipMallocAsync on `stream` and released with hipFreeAsync on the same
+ * stream (no host synchronisation). Returns FA_ERR_OUT_OF_MEMORY if it cannot
+ * be had.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+           const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+           int B, int H, int N, int d, int causal, float softmax_scale,
+           void* stream);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Diagnostics: the name of the HIP error behind the most recent FA_ERR_HIP or
+ * FA_ERR_OUT_OF_MEMORY returned on the calling thread ("hipSuccess" if none).
+ * The string is static; the value is per thread.
+ */
+const char* fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

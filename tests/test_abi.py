@@ -1,0 +1,113 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the header
+declares, and rejects invalid arguments on the host before any HIP call (so
+these calls are safe without a GPU: nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_17_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# A fake but 16-byte aligned, non-null "device pointer": validation never
+# dereferences pointers and every call below fails validation first.
+P = 0x10000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == ["fa_bwd", "fa_fwd", "fa_last_hip_error", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings():
+    assert fa.fa_status_string(fa.FA_OK).startswith("FA_OK")
+    for st in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, fa.FA_ERR_OUT_OF_MEMORY):
+        assert fa.fa_status_string(st).startswith("FA_ERR")
+    assert fa.fa_status_string(12345) == "unknown fa_status"
+    assert fa.fa_last_hip_error() == "hipSuccess"
+
+
+GOOD = dict(B=1, H=2, N=16, d=128, causal=0, softmax_scale=0.125)
+
+
+def fwd(**kw):
+    a = dict(GOOD, Q=P, K=P, V=P, O=P, LSE=P, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["d"],
+                     a["causal"], a["softmax_scale"], a["stream"])
+
+
+def bwd(**kw):
+    a = dict(GOOD, Q=P, K=P, V=P, O=P, LSE=P, dO=P, dQ=P, dK=P, dV=P, stream=None)
+    a.update(kw)
+    return fa.fa_bwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["dO"], a["dQ"], a["dK"], a["dV"],
+                     a["B"], a["H"], a["N"], a["d"], a["causal"], a["softmax_scale"], a["stream"])
+
+
+BAD_SHAPES = [
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_INVALID_ARG),          # N * d >= 2^31
+    (dict(B=1 << 16, H=1 << 16, N=64), fa.FA_ERR_INVALID_ARG),  # grid too large
+]
+
+
+@pytest.mark.parametrize("kw,want", BAD_SHAPES, ids=lambda x: str(x))
+def test_fwd_rejects_bad_shapes(kw, want):
+    assert fwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", BAD_SHAPES, ids=lambda x: str(x))
+def test_bwd_rejects_bad_shapes(kw, want):
+    assert bwd(**kw) == want
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "V", "O"])
+def test_fwd_rejects_null_and_misaligned(name):
+    assert fwd(**{name: None}) == fa.FA_ERR_INVALID_ARG
+    assert fwd(**{name: P + 8}) == fa.FA_ERR_INVALID_ARG
+
+
+def test_fwd_lse_alignment():
+    assert fwd(LSE=P + 2) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "V", "O", "dO", "dQ", "dK", "dV", "LSE"])
+def test_bwd_rejects_null_and_misaligned(name):
+    assert bwd(**{name: None}) == fa.FA_ERR_INVALID_ARG
+    assert bwd(**{name: P + 2}) == fa.FA_ERR_INVALID_ARG
+
+
+def test_torch_wrapper_checks_before_calling():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        fa.forward(q.float(), q, q)
+    with pytest.raises(ValueError):
+        fa.forward(q, q[:, :, :2], q)
+    with pytest.raises(ValueError):
+        fa.forward(q[..., ::2], q[..., ::2], q[..., ::2])

@@ -1,0 +1,199 @@
+"""GPU parity: fa_fwd / fa_bwd (through the C ABI) against the CPU fp64 oracle.
+
+Small shapes spanning several tiles and ragged tails are compared element by
+element over every output. The five named workloads run at full size in the
+launch configuration the benchmark times; there the oracle checks every head
+at sampled rows (forward), whole sampled heads (forward and backward), and
+two backward identities over every head.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from tests.gpu_util import (GRAD_RTOL, LSE_ATOL, O_ATOL, announce, max_abs, rel_to_max,
+                            to_dev, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(fa, x, causal, scale, backward):
+    import torch
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    o, lse = fa.forward(q, k, v, causal, scale)
+    out = {"o": o, "lse": lse}
+    if backward:
+        do = to_dev(x["do"])
+        out["dq"], out["dk"], out["dv"] = fa.backward(do, q, k, v, o, lse, causal, scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _dec(x):
+    return {k: oracle.bf16_bits_to_f64(v) for k, v in x.items()}
+
+
+SMALL_N = [1, 2, 3, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 513]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_small_shapes_every_element(fa, N, causal, d):
+    B, H = 1, 2
+    seed = 1000 + N * 4 + 2 * int(causal) + (d == 128)
+    x = ai.make_qkv(B, H, N, d, seed, with_do=True)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    announce(f"small N={N} d={d} causal={causal} seed={seed}")
+    g = _run(fa, x, causal, scale, backward=True)
+    f = _dec(x)
+    o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal, scale)
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], causal, scale)
+    assert max_abs(to_f64(g["o"]), o_ref) <= O_ATOL
+    assert max_abs(to_f64(g["lse"]), lse_ref) <= LSE_ATOL
+    for name, ref in (("dq", dq_ref), ("dk", dk_ref), ("dv", dv_ref)):
+        err = rel_to_max(to_f64(g[name]), ref) if np.max(np.abs(ref)) > 0 else max_abs(to_f64(g[name]), ref)
+        assert err <= GRAD_RTOL, (name, err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [200, 1000])
+def test_large_logits_rescale(fa, N, causal):
+    """Q, K ~ N(0, 3^2): near one-hot rows and a running max that keeps moving."""
+    x = ai.make_qkv(2, 2, N, 128, 77 + N, sigma_qk=3.0, with_do=True)
+    scale = float(np.float32(1.0 / math.sqrt(128)))
+    announce(f"large-logit N={N} causal={causal}")
+    g = _run(fa, x, causal, scale, backward=True)
+    f = _dec(x)
+    o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal, scale)
+    grads = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], causal, scale)
+    assert max_abs(to_f64(g["o"]), o_ref) <= O_ATOL
+    assert max_abs(to_f64(g["lse"]), lse_ref) <= LSE_ATOL
+    for name, ref in zip(("dq", "dk", "dv"), grads):
+        assert rel_to_max(to_f64(g[name]), ref) <= GRAD_RTOL, name
+
+
+def test_closed_forms_on_gpu(fa):
+    """Identical keys give the mean of the visible values; N=1 gives O = V."""
+    import torch
+    rng = np.random.default_rng(5)
+    B, H, N, d = 1, 2, 300, 128
+    x = ai.make_qkv(B, H, N, d, 9)
+    x["k"] = np.broadcast_to(x["k"][:, :, :1], x["k"].shape).copy()
+    scale = 0.0883883461356163
+    announce("closed forms")
+    g = _run(fa, x, True, scale, backward=False)
+    v = oracle.bf16_bits_to_f64(x["v"])
+    cnt = np.arange(1, N + 1)[None, None, :, None]
+    mean = np.cumsum(v, axis=2) / cnt
+    assert max_abs(to_f64(g["o"]), mean) <= O_ATOL
+    y = ai.make_qkv(3, 2, 1, 64, 10)
+    g1 = _run(fa, y, False, 0.125, backward=False)
+    assert np.array_equal(to_f64(g1["o"]), oracle.bf16_bits_to_f64(y["v"]))
+    del rng, torch
+
+
+def test_forward_is_deterministic_and_lse_optional(fa):
+    import torch
+    x = ai.make_qkv(2, 3, 700, 128, 11)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    announce("determinism")
+    o1, l1 = fa.forward(q, k, v, True)
+    o2, l2 = fa.forward(q, k, v, True)
+    o3, _ = fa.forward(q, k, v, True, need_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+
+
+def test_side_stream(fa):
+    import torch
+    x = ai.make_qkv(1, 4, 333, 64, 12, with_do=True)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    announce("side stream")
+    ref_o, ref_l = fa.forward(q, k, v, True)
+    ref = fa.backward(do, q, k, v, ref_o, ref_l, True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = fa.forward(q, k, v, True)
+        grads = fa.backward(do, q, k, v, o, l, True)
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    for a, b in zip(grads, ref):
+        assert (a.float() - b.float()).abs().max().item() <= 2e-2 * b.float().abs().max().item()
+
+
+# --- full-size workloads --------------------------------------------------------
+
+def _sample_heads(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (B - 1, H - 1)}
+    while len(heads) < min(n, B * H):
+        heads.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(heads)
+
+
+def _check_workload(fa, wname):
+    import torch
+    w = ai.WORKLOADS[wname]
+    announce(f"workload {wname} {w.label} generating inputs")
+    x = ai.make_inputs(w)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    small = B * H * N * N <= 4 * 32 * 1024 * 1024  # whole-tensor oracle is cheap
+    heads = [(b, h) for b in range(B) for h in range(H)] if small else _sample_heads(B, H, 6, w.seed)
+    rng = np.random.default_rng(100 + w.seed)
+    for causal in w.causal_modes:
+        announce(f"workload {wname} causal={causal} on GPU")
+        g = _run(fa, x, causal, w.scale, backward=w.backward)
+        o, lse = to_f64(g["o"]), to_f64(g["lse"])
+        # every head at sampled rows (row 0 and N-1 always)
+        for b in range(B):
+            for h in range(H):
+                rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 6)]))
+                qb = oracle.bf16_bits_to_f64(x["q"][b, h, rows])
+                kb = oracle.bf16_bits_to_f64(x["k"][b, h])
+                vb = oracle.bf16_bits_to_f64(x["v"][b, h])
+                ro, rl = oracle.rows_forward(qb, kb, vb, rows, causal, w.scale)
+                assert max_abs(o[b, h, rows], ro) <= O_ATOL, (wname, b, h)
+                assert max_abs(lse[b, h, rows], rl) <= LSE_ATOL, (wname, b, h)
+        # whole heads
+        for b, h in heads:
+            fq, fk, fv = (oracle.bf16_bits_to_f64(x[n][b, h]) for n in ("q", "k", "v"))
+            ro, rl = oracle.head_forward(fq, fk, fv, causal, w.scale)
+            assert max_abs(o[b, h], ro) <= O_ATOL, (wname, b, h)
+            assert max_abs(lse[b, h], rl) <= LSE_ATOL, (wname, b, h)
+            if w.backward:
+                fdo = oracle.bf16_bits_to_f64(x["do"][b, h])
+                rq, rk, rv = oracle.head_backward(fq, fk, fv, fdo, causal, w.scale)
+                for name, ref in (("dq", rq), ("dk", rk), ("dv", rv)):
+                    err = rel_to_max(to_f64(g[name][b, h]), ref)
+                    assert err <= GRAD_RTOL, (wname, name, b, h, err)
+        if w.backward:
+            # identities over every head, in float64 on the device:
+            # sum_j dV_j = sum_i dO_i and <dQ, Q> = <dK, K>
+            do = to_dev(x["do"]).double()
+            dv_sum = g["dv"].double().sum(2)
+            do_sum = do.sum(2)
+            r1 = ((dv_sum - do_sum).abs().amax(-1) / do_sum.abs().amax(-1)).max().item()
+            q, k = to_dev(x["q"]).double(), to_dev(x["k"]).double()
+            a = (g["dq"].double() * q).sum((2, 3))
+            bb = (g["dk"].double() * k).sum((2, 3))
+            den = torch.maximum((g["dq"].double().abs() * q.abs()).sum((2, 3)),
+                                (g["dk"].double().abs() * k.abs()).sum((2, 3)))
+            r2 = ((a - bb).abs() / den).max().item()
+            announce(f"identities {wname}: sum dV {r1:.2e}, <dQ,Q>-<dK,K> {r2:.2e}")
+            assert r1 <= 2e-2 and r2 <= 1e-2
+        del g
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wname", ["c1", "c2"])
+def test_workload_small(fa, wname):
+    _check_workload(fa, wname)
+
+
+@pytest.mark.parametrize("wname", ["c3", "c4", "c5"])
+def test_workload_full_size(fa, wname):
+    _check_workload(fa, wname)
