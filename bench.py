@@ -1,0 +1,179 @@
+"""Throughput of exact tiled attention (fa_fwd + fa_bwd) on one MI355X.
+
+One step is the whole hot path over one batch: the forward (O, LSE) and the
+backward (dQ, dK, dV) of causal bf16 attention at B=4, H=64, N=4096, d=128
+with Q, K ~ N(0, 3^2) and V, dO ~ N(0, 1) (synthetic, seeded). Inputs are
+resident in HBM before the timed region starts.
+
+FLOPs are counted algorithmically: 4 B H N^2 d for the forward, halved when
+causal, and 2.5 times that for the backward. The printed JSON line carries:
+  value      whole-step (fwd + bwd) TFLOP/s
+  fwd_*      the forward alone, the figure the 50%-of-peak target is set on
+  roofline   the dominant launch (the one with the largest time share),
+             timed live with HIP events on the stream it runs on
+  cpu_baseline  the CPU fp64 oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0
+
+# Page 4 ("RTX Flash Attention Implementation COMPLETE", Performance
+# Specifications) times for the same shapes on another GPU; context only.
+PAGE_TIMES_MS = {"2x8x512x64": 0.85, "4x32x1024x128": 2.1, "8x64x2048x128": 8.3,
+                 "4x64x4096x128": 15.2}
+
+
+def flops(w, causal):
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    if causal:
+        f *= 0.5
+    return f, 2.5 * f
+
+
+def cpu_baseline(w, causal, budget_s=15.0):
+    """The fp64 oracle (as it stands) on whole heads of the same workload."""
+    import numpy as np
+    import attn_inputs as ai
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((int(i.get("num_threads", 1)) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    f_fwd_head = 4.0 * w.N * w.N * w.d * (0.5 if causal else 1.0)
+    f_head = 3.5 * f_fwd_head
+    x = ai.make_qkv(1, 1, w.N, w.d, w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v, with_do=True)
+    heads, t_total = 0, 0.0
+    while t_total < budget_s and heads < 64:
+        q, k, v, do = (oracle.bf16_bits_to_f64(x[n][0, 0]) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        oracle.head_forward(q, k, v, causal, w.scale)
+        oracle.head_backward(q, k, v, do, causal, w.scale)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    return {"value": heads * f_head / t_total / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads} whole head(s) of {w.label} causal={causal}, fwd+bwd in fp64 "
+                      f"({t_total:.1f} s); FLOPs counted like the GPU line (the oracle does "
+                      f"the full N^2 work)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", help="attn_inputs workload name")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true", help="time only fa_fwd (profiling aid)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
+              "is independent, so N GPUs would each run this same kernel on B*H/N heads.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import attn_inputs as ai
+    import exact_tiled_attention_17_amd as fa
+
+    w = ai.WORKLOADS[args.workload]
+    causal = True if True in w.causal_modes else False
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = ai.make_qkv(w.B, w.H, w.N, w.d, w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v,
+                    with_do=True)
+    t = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in x}
+    del x
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.forward(q, k, v, causal, w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if not args.fwd_only:
+            fa.backward(do, q, k, v, o, lse, causal, w.scale, dq=dq, dk=dk, dv=dv)
+            if ev is not None:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if not args.fwd_only else [0.0]
+    f_fwd, f_bwd = flops(w, causal)
+    ms_step = wall * 1e3 / args.steps
+    t_fwd = float(np.mean(fwd_ms))
+    t_bwd = float(np.mean(bwd_ms))
+    fwd_tf = f_fwd / (t_fwd * 1e-3) / 1e12
+    bwd_tf = f_bwd / (t_bwd * 1e-3) / 1e12 if t_bwd > 0 else 0.0
+    step_flops = f_fwd + (0.0 if args.fwd_only else f_bwd)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    if t_bwd >= t_fwd:
+        name, fl, tms = "fa_bwd (bwd_pre_kernel + bwd_kernel + bwd_dq_kernel)", f_bwd, t_bwd
+    else:
+        name, fl, tms = "fa_fwd (fwd_kernel)", f_fwd, t_fwd
+    achieved = fl / (tms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(tms, 4)}
+
+    out = {
+        "metric": "bf16 attention TFLOP/s fwd & fwd+bwd at 4x64x4096x128 causal, % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"attention fwd+bwd, causal={causal}, B={w.B} H={w.H} N={w.N} "
+                               f"d={w.d}, Q,K~N(0,{w.sigma_qk:g}^2), V,dO~N(0,1), seed {w.seed}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+                   "fwd_only": args.fwd_only},
+        "fwd_ms": round(t_fwd, 4),
+        "bwd_ms": round(t_bwd, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "fwd_pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+        "fwd_bwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "page_context_ms": PAGE_TIMES_MS.get(w.label),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, causal)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
