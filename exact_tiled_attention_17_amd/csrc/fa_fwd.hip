@@ -25,7 +25,13 @@
 //    cross the diagonal or the end of the sequence.
 //  * The softmax runs in base 2 in float32: c = scale * log2(e) is folded into
 //    one FMA per score; P is rounded to bf16 for the matrix core and the row
-//    sum l is accumulated from those same rounded values (dot2 with 1s).
+//    sum l is accumulated from those same rounded values (dot2 with 1s). The
+//    reference max only moves when the row max outgrows it by 2^8, so the
+//    O^T rescale runs on few tiles.
+//  * Global reads go through buffer resources: rows past the end of the
+//    sequence read as zeros, with no branches around the loads.
+//  * The two waves sharing a SIMD raise their priority in their matrix-core
+//    phases, so one wave's softmax overlaps the other's products.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -53,6 +59,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 float* __restrict__ LSE, int N, int BH, float c_log2) {
   using C = FwdCfg<D, NW>;
   constexpr int BR = C::BR, BC = C::BC, CH = C::CH, VTS = C::VTS;
+  // Lazy rescaling: the running max used for P only moves when the true row
+  // max exceeds it by more than TAU (base-2 units), so P <= 2^TAU and the
+  // O^T rescale is skipped on most tiles. The result is exact either way:
+  // O = sum_j 2^(c s_j - m) v_j / sum_j 2^(c s_j - m) for any common m.
+  constexpr float TAU = 8.f;
   __shared__ __attribute__((aligned(16))) __bf16 ks[2][BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 vt[2][D * VTS];
 
@@ -68,9 +79,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int hh = lane >> 5;
 
   const size_t head = (size_t)bh * (size_t)N * D;
-  const __bf16* Qh = Q + head;
-  const __bf16* Kh = K + head;
-  const __bf16* Vh = V + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto rQ = make_rsrc(Q + head, head_bytes);
+  const auto rK = make_rsrc(K + head, head_bytes);
+  const auto rV = make_rsrc(V + head, head_bytes);
 
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * wave;  // first query row of this wave
@@ -81,19 +93,28 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const bool wave_active = wrow0 < N;
   const int jw_last = CAUSAL ? min(wrow0 + 31, N - 1) / BC : nkv - 1;
 
-  // ---- Q^T operand: lane holds row `row`, d = 16 s + 8 hh .. +7 -------------
+  // ---- Q^T operand: lane holds row `row`, d = 16 s + 8 hh .. +7 (0 past N) --
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < N) v = ld_global16(Qh + (size_t)row * D + 16 * s + 8 * hh);
-    qf[s] = as_bf16x8(v);
-  }
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
 
   // ---- K/V tile staging -----------------------------------------------------
-  const bool k_loader = tid < C::LOADERS;
+  // K loaders: chunk i -> (key i / CH, 16-byte chunk i % CH), rows contiguous.
+  // V loaders: group g -> (4 keys from 4 kg, chunk dc); within 16 lanes, 4 key
+  // groups x 4 chunks, so the transposed 8-byte LDS writes spread over banks
+  // while each global read still covers 64 contiguous bytes of a row.
+  const bool k_loader = wave < NW / 2;  // wave-uniform: a scalar branch
   const int lt = k_loader ? tid : tid - C::LOADERS;
   u32x4 stg[C::KPT];
+  auto v_group = [&](int g, int& kg, int& dc) {
+    constexpr int DCH = CH / 4;  // dc_hi range
+    const int dc_lo = g & 3, kg_lo = (g >> 2) & 3;
+    const int rest = g >> 4;
+    const int dc_hi = rest % DCH, kg_hi = rest / DCH;
+    dc = dc_hi * 4 + dc_lo;
+    kg = kg_hi * 4 + kg_lo;
+  };
 
   auto load_tile = [&](int j) {
     const int kv0 = j * BC;
@@ -102,22 +123,16 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int r = 0; r < C::KPT; ++r) {
         const int i = lt + r * C::LOADERS;
         const int key = i / CH, c = i % CH;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (kv0 + key < N) v = ld_global16(Kh + (size_t)(kv0 + key) * D + 8 * c);
-        stg[r] = v;
+        stg[r] = buf_load16(rK, (uint32_t)(kv0 + key) * (D * 2) + c * 16);
       }
     } else {
 #pragma unroll
       for (int r = 0; r < C::VPT; ++r) {
-        const int g = lt + r * C::LOADERS;
-        const int kg = g / CH, dc = g % CH;
+        int kg, dc;
+        v_group(lt + r * C::LOADERS, kg, dc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 4 * kg + i;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (kv0 + key < N) v = ld_global16(Vh + (size_t)(kv0 + key) * D + 8 * dc);
-          stg[4 * r + i] = v;
-        }
+        for (int i = 0; i < 4; ++i)
+          stg[4 * r + i] = buf_load16(rV, (uint32_t)(kv0 + 4 * kg + i) * (D * 2) + dc * 16);
       }
     }
   };
@@ -132,8 +147,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     } else {
 #pragma unroll
       for (int r = 0; r < C::VPT; ++r) {
-        const int g = lt + r * C::LOADERS;
-        const int kg = g / CH, dc = g % CH;
+        int kg, dc;
+        v_group(lt + r * C::LOADERS, kg, dc);
         u32x2 col[8];
         transpose4x8(stg[4 * r], stg[4 * r + 1], stg[4 * r + 2], stg[4 * r + 3], col);
         const int pos = kperm(4 * kg);
@@ -147,12 +162,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   f32x16 o[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
-  float m_run = -INFINITY;  // running max of c * s over the row (base-2 units)
+  float m_run = -INFINITY;  // reference max of c * s for this row (base-2 units)
   float l_run = 0.f;        // this lane's share of the running sum
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   load_tile(0);
   store_tile(0);
+  wait_vmem_all();
   __syncthreads();
 
   for (int j = 0; j < nkv; ++j) {
@@ -160,19 +176,21 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (j + 1 < nkv) load_tile(j + 1);
 
     if (wave_active && j <= jw_last) {
-      // S^T = K_j Q^T : two 32-key blocks
+      // S^T = K_j Q^T : two 32-key blocks, interleaved accumulation chains
+      __builtin_amdgcn_s_setprio(1);
       f32x16 s[BC / 32];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        s[kb] = f32x16{};
-        const int key = 32 * kb + l32;
+      for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
+      for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb) {
+          const int key = 32 * kb + l32;
           const int c = 2 * st + hh;
           const bf16x8 a = ld_lds16(&ks[buf][key * D + ((c ^ (key & (CH - 1))) * 8)]);
           s[kb] = mfma32(a, qf[st], s[kb]);
         }
-      }
+      __builtin_amdgcn_s_setprio(0);
       // masks: causal (key > row) and sequence end (key >= N), only where needed
       const int kv0 = j * BC;
       const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
@@ -185,16 +203,22 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             if (key >= N || (CAUSAL && key > row)) s[kb][r] = -INFINITY;
           }
       }
-      // online softmax (base 2)
+      // online softmax (base 2) with lazy rescaling
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+      mx = pair_max(mx) * c_log2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+      }
+      const float neg_m = -m_run;
 
       u32x4 pf[BC / 16];
       float lsum = 0.f;
@@ -204,24 +228,24 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e], c_log2, -m_new));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e + 1], c_log2, -m_new));
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e], c_log2, neg_m));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e + 1], c_log2, neg_m));
             const uint32_t pk = pack_bf16(p0, p1);
             pf[2 * kb + t][e] = pk;
             lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
           }
-      l_run = l_run * alpha + lsum;
+      l_run += lsum;
 
-      // O^T = alpha * O^T + V^T P^T
+      // O^T += V^T P^T
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
-        o[b] *= alpha;
+      for (int t = 0; t < BC / 16; ++t)
 #pragma unroll
-        for (int t = 0; t < BC / 16; ++t) {
+        for (int b = 0; b < D / 32; ++b) {
           const bf16x8 a = ld_lds16(&vt[buf][(32 * b + l32) * VTS + 16 * t + 8 * hh]);
           o[b] = mfma32(a, as_bf16x8(pf[t]), o[b]);
         }
-      }
+      __builtin_amdgcn_s_setprio(0);
     }
 
     if (j + 1 < nkv) store_tile(buf ^ 1);
