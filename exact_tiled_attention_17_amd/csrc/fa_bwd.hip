@@ -8,14 +8,18 @@
 //
 //  1. bwd_pre_kernel: per query row, D_i = dO_i . O_i (float32) and the LSE in
 //     base 2; zeroes the float32 dQ accumulator.
-//  2. bwd_kernel: one workgroup per (batch, head, block of 128 keys); each of
-//     its 4 waves keeps 32 keys' K and V rows in registers and their dK, dV
-//     accumulators in float32 for the whole sweep over query tiles of BRB rows.
-//     Per query tile, on 32x32x16 bf16 matrix cores:
-//        S = Q K^T, dP = dO V^T        (lane = one key, 16 queries per block)
+//  2. bwd_kernel: one workgroup per (batch, head, block of 128 keys); each
+//     32-key block has a P-wave (dV) and a dS-wave (dK) on one SIMD, holding
+//     float32 accumulators for the whole sweep over query tiles of 32 rows.
+//     The K block and the Q, dO tiles sit row-major in LDS; operands that need
+//     them transposed use gfx950's transposing LDS read instead of a second,
+//     transposed copy. Per query tile, on 32x32x16 bf16 matrix cores:
+//        S = Q K^T, dP = dO V^T        (lane = one key, 16 queries)
 //        P = exp2(c S - LSE2), dS = P (dP - D)
 //        dV += P^T dO, dK += dS^T Q    (P^T, dS^T straight from registers)
-//        dQ += dS K                    (dS through LDS, float32 atomics)
+//        dQ += dS K                    (dS^T through LDS, float32 atomics)
+//     dQ of a step runs during the next step's S/dP products (query-side
+//     tiles double-buffered), so each step has one barrier.
 //     Causal: query tiles that see none of the block's keys are skipped.
 //  3. bwd_dq_kernel: dQ = bf16(scale * dQ_acc).
 //
@@ -61,46 +65,63 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 // ---------------------------------------------------------------------------
 // 2. Main backward kernel
 // ---------------------------------------------------------------------------
-template <int D, int BRB_>
+template <int D>
 struct BwdCfg {
-  static constexpr int NW = 4;
-  static constexpr int BCB = 32 * NW;  // keys per workgroup
-  static constexpr int BRB = BRB_;     // queries per step
-  static constexpr int QB = BRB / 32;  // 32-query blocks per step
-  static constexpr int CH = D / 8;
-  static constexpr int KTS = BCB + 8;  // padded row length of K^T in LDS
-  static constexpr int QTS = BRB + 8;  // padded row length of Q^T, dO^T in LDS
-  static constexpr int DSS = BCB + 8;  // padded row length of dS in LDS
-  static constexpr int NDB = D / 32;   // 32-wide column blocks of d
-  static constexpr int KSPLIT = NW / NDB;       // waves sharing one dQ column block
-  static constexpr int DQ_KEYS = BCB / KSPLIT;  // keys each wave sums for dQ
-  // Query-tile loading: per tensor (Q, dO), (BRB/4) row groups x CH chunks;
-  // half of the loader waves take Q, the other half dO.
-  static constexpr int TG = (BRB / 4) * CH;                 // groups per tensor
-  static constexpr int LWT = TG >= 64 * (NW / 2) ? NW / 2 : (TG + 63) / 64;  // waves per tensor
-  static constexpr int GPT = TG / (64 * LWT);               // groups per loader thread
-  static_assert(GPT >= 1 && GPT * 64 * LWT == TG, "tile loaders");
+  static constexpr int KBLK = 4;            // 32-key blocks per workgroup
+  static constexpr int NW = 2 * KBLK;       // a P-wave and a dS-wave per key block
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BCB = 32 * KBLK;     // keys per workgroup
+  static constexpr int BRB = 32;            // queries per step
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int NDB = D / 32;        // 32-wide column blocks of d
+  static constexpr int KSPLIT = KBLK / NDB;       // P-waves sharing one dQ column block
+  static constexpr int DQ_KEYS = BCB / KSPLIT;    // keys each P-wave sums for dQ
+  static constexpr int TPT = 2 * BRB * CH / THREADS;  // Q/dO tile chunks per thread
+  static constexpr int KPT = BCB * CH / THREADS;      // K-block chunks per thread
+  static_assert(TPT >= 1 && KPT >= 1 && KSPLIT >= 1, "work split");
 };
 
-template <int D, int BRB_, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// Row-major tiles of d-wide rows keep 16-byte chunk c of row r at chunk
+// position c ^ swz(r). For d = 128 the swizzle makes both access patterns
+// conflict-free: 16 consecutive rows at one chunk (operand rows), and 4
+// consecutive rows x 4 consecutive chunks (transposing reads).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {  // element offset of (r, col), col % 4 == 0
+  return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 4);
+}
+// dS^T tile: [128 keys][32 queries], 8-byte units u of row r at u ^ ((r >> 2) & 7):
+// conflict-free both for a wave's 8-byte column writes and for transposing reads.
+__device__ __forceinline__ int dst_off(int r, int col) {
+  return r * 32 + ((((col >> 2) ^ (r >> 2)) & 7) << 2);
+}
+
+// Each 32-key block of the workgroup is served by two waves on one SIMD:
+//   P-wave:  S = Q K^T, P = exp2(c S - LSE2), dV += P^T dO, and (one step
+//            late) dQ += dS K for its column block, with float32 atomics;
+//   dS-wave: dP = dO V^T, dS = P (dP - D) with P from its partner through
+//            LDS, dK += dS^T Q, and dS^T into LDS for the dQ products.
+// Splitting the dK and dV accumulators keeps each wave under 256 registers,
+// so two waves share a SIMD and one's softmax overlaps the other's products.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                 const f32x2* __restrict__ rowstat, float* __restrict__ dq_acc,
                 __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH,
                 float c_log2, float scale) {
-  using C = BwdCfg<D, BRB_>;
-  constexpr int BCB = C::BCB, BRB = C::BRB, QB = C::QB, CH = C::CH;
-  constexpr int KTS = C::KTS, QTS = C::QTS, DSS = C::DSS;
-  __shared__ __attribute__((aligned(16))) __bf16 kt[D * KTS];
-  // Query tiles are single-buffered: the next tile is written after the
-  // mid-step barrier, when every wave has finished reading the current one.
-  __shared__ __attribute__((aligned(16))) __bf16 qs[BRB * D];
-  __shared__ __attribute__((aligned(16))) __bf16 dos[BRB * D];
-  __shared__ __attribute__((aligned(16))) __bf16 qtr[D * QTS];
-  __shared__ __attribute__((aligned(16))) __bf16 dotr[D * QTS];
-  __shared__ __attribute__((aligned(16))) __bf16 dss[BRB * DSS];
-  __shared__ __attribute__((aligned(16))) f32x2 rs[BRB];
+  using C = BwdCfg<D>;
+  constexpr int BCB = C::BCB, BRB = C::BRB, CH = C::CH;
+  __shared__ __attribute__((aligned(16))) __bf16 ks[BCB * D];         // K block, row-major
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2][BRB * D];      // Q tiles
+  __shared__ __attribute__((aligned(16))) __bf16 dos[2][BRB * D];     // dO tiles
+  __shared__ __attribute__((aligned(16))) __bf16 dsts[2][BCB * BRB];  // dS^T tiles
+  __shared__ __attribute__((aligned(16))) f32x4 ps[C::KBLK][4][64];   // P, lane-major
+  __shared__ __attribute__((aligned(16))) f32x2 rs[2][BRB];           // (LSE2, D) per query
 
   const int nkb = (N + BCB - 1) / BCB;
   int bh, kb;
@@ -111,6 +132,12 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  const bool pwave = wave < C::KBLK;           // role (wave-uniform)
+  const int kblk = pwave ? wave : wave - C::KBLK;
+  // transposing-read addressing of this lane (see ld_lds_tr)
+  const int tr_grp = lane >> 4, tr_i = lane & 15;
+  const int tr_e = tr_i >> 2;                              // which k-slot row it fetches
+  const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);   // column within a 32-block
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -122,220 +149,192 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rRS = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 8u);
 
   const int k0 = kb * BCB;
-  const int kw0 = k0 + 32 * wave;  // this wave's first key
+  const int kw0 = k0 + 32 * kblk;  // this wave's first key
   const int key = kw0 + l32;       // this lane's key (column of S)
 
-  // K and V rows of this lane's key as B operands: d = 16 s + 8 hh .. +7 (0 past N)
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K rows (P-wave) or V rows (dS-wave) of this lane's key as B operands (0 past N)
+  bf16x8 frag[D / 16];
+  {
+    const auto rF = pwave ? rK : rV;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const uint32_t off = (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2;
-    kf[s] = as_bf16x8(buf_load16(rK, off));
-    vf[s] = as_bf16x8(buf_load16(rV, off));
+    for (int s = 0; s < D / 16; ++s)
+      frag[s] = as_bf16x8(buf_load16(rF, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
   }
-  // K^T of the whole block in LDS (natural key order), for dQ = dS K
-  for (int g = tid; g < (BCB / 4) * CH; g += 256) {
-    const int kg = g / CH, dc = g % CH;
-    u32x4 r[4];
+  // K block into LDS (row-major, swizzled) for the dQ products
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r[i] = buf_load16(rK, (uint32_t)(k0 + 4 * kg + i) * (D * 2) + dc * 16);
-    u32x2 col[8];
-    transpose4x8(r[0], r[1], r[2], r[3], col);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st_lds8(&kt[(8 * dc + e) * KTS + 4 * kg], col[e]);
+  for (int r = 0; r < C::KPT; ++r) {
+    const int i = tid + r * C::THREADS;
+    const int kr = i / CH, c = i % CH;
+    st_lds16(&ks[tile_off<D>(kr, 8 * c)], buf_load16(rK, (uint32_t)(k0 + kr) * (D * 2) + c * 16));
   }
 
-  // Query-tile loaders (wave-uniform roles)
-  const bool tile_loader = wave < 2 * C::LWT;
-  const bool loads_q = wave < C::LWT;
-  const int tbase = (wave % C::LWT) * 64 + lane;
-  const auto rT = loads_q ? rQ : rdO;
-  u32x4 stg[4 * C::GPT];
-  f32x2 rstg = {INFINITY, 0.f};
-  const bool rs_loader = wave == C::NW - 1 && lane < BRB;
-
+  // Q / dO tile loaders: P-waves load Q, dS-waves dO
+  const int tl = tid % (C::THREADS / 2);
+  const auto rT = pwave ? rQ : rdO;
+  u32x4 stg[C::TPT];
+  f32x2 rstg = {0.f, 0.f};
   auto load_q = [&](int i) {
     const int q0 = i * BRB;
-    if (tile_loader) {
 #pragma unroll
-      for (int gi = 0; gi < C::GPT; ++gi) {
-        const int g = tbase + gi * 64 * C::LWT;
-        const int qg = g / CH, dc = g % CH;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          stg[4 * gi + r] = buf_load16(rT, (uint32_t)(q0 + 4 * qg + r) * (D * 2) + dc * 16);
-      }
+    for (int r = 0; r < C::TPT; ++r) {
+      const int j = tl + r * (C::THREADS / 2);
+      stg[r] = buf_load16(rT, (uint32_t)(q0 + j / CH) * (D * 2) + (j % CH) * 16);
     }
-    if (wave == C::NW - 1) {
-      // one row per lane; rows past the end get LSE2 = +inf, D = 0, so P = dS = 0
-      const int q = q0 + lane;
-      const u32x2 v = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rRS, (uint32_t)q * 8u, 0, 0));
-      rstg = q < N ? __builtin_bit_cast(f32x2, v) : f32x2{INFINITY, 0.f};
-    }
+    if (wave == C::NW - 1)
+      rstg = __builtin_bit_cast(
+          f32x2, __builtin_amdgcn_raw_buffer_load_b64(rRS, (uint32_t)(q0 + lane) * 8u, 0, 0));
   };
-  auto store_q = [&]() {
-    if (tile_loader) {
-      __bf16* rm = loads_q ? qs : dos;
-      __bf16* tr = loads_q ? qtr : dotr;
+  auto store_q = [&](int i, int buf) {
+    __bf16* t = pwave ? qs[buf] : dos[buf];
 #pragma unroll
-      for (int gi = 0; gi < C::GPT; ++gi) {
-        const int g = tbase + gi * 64 * C::LWT;
-        const int qg = g / CH, dc = g % CH;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = 4 * qg + r;
-          st_lds16(&rm[q * D + ((dc ^ (q & (CH - 1))) * 8)], stg[4 * gi + r]);
-        }
-        u32x2 col[8];
-        transpose4x8(stg[4 * gi], stg[4 * gi + 1], stg[4 * gi + 2], stg[4 * gi + 3], col);
-        const int pos = kperm(4 * qg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st_lds8(&tr[(8 * dc + e) * QTS + pos], col[e]);
-      }
+    for (int r = 0; r < C::TPT; ++r) {
+      const int j = tl + r * (C::THREADS / 2);
+      st_lds16(&t[tile_off<D>(j / CH, 8 * (j % CH))], stg[r]);
     }
-    if (rs_loader) rs[lane] = rstg;
+    // rows past the end get LSE2 = +inf and D = 0, so their P and dS are 0
+    if (wave == C::NW - 1 && lane < BRB)
+      rs[buf][lane] = i * BRB + lane < N ? rstg : f32x2{INFINITY, 0.f};
   };
 
-  f32x16 dk[D / 32], dv[D / 32];
+  // dQ[q0.., 32 db ..] += dS K for the step whose dS^T sits in dsts[buf]
+  // (P-waves; M = queries, N = d, k = keys in natural order; both operands
+  // read transposed: dS from dS^T, K from the K block)
+  const int db = kblk % C::NDB;
+  const int dq_k0 = (kblk / C::NDB) * C::DQ_KEYS;
+  auto dq_step = [&](int q0, int buf) {
+    f32x16 acc = f32x16{};
 #pragma unroll
-  for (int b = 0; b < D / 32; ++b) {
-    dk[b] = f32x16{};
-    dv[b] = f32x16{};
-  }
+    for (int t = 0; t < C::DQ_KEYS / 16; ++t) {
+      const int r_lo = dq_k0 + 16 * t + 8 * hh + tr_e;
+      const int r_hi = r_lo + 4;
+      const bf16x8 a = cat8(ld_lds_tr(&dsts[buf][dst_off(r_lo, tr_col)]),
+                            ld_lds_tr(&dsts[buf][dst_off(r_hi, tr_col)]));
+      const bf16x8 b = cat8(ld_lds_tr(&ks[tile_off<D>(r_lo, 32 * db + tr_col)]),
+                            ld_lds_tr(&ks[tile_off<D>(r_hi, 32 * db + tr_col)]));
+      acc = mfma32(a, b, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      buf_atomic_add(rdQ, ((uint32_t)q * D + 32 * db + l32) * 4u, acc[r]);
+    }
+  };
+
+  // this wave's accumulator: dV (P-wave) or dK (dS-wave), M = keys, N = d
+  f32x16 acc_kd[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) acc_kd[b] = f32x16{};
 
   const int nqt = (N + BRB - 1) / BRB;
   const int i0 = CAUSAL ? k0 / BRB : 0;
   const int nsteps = nqt - i0;
-  // dQ work split of this wave: column block and key range
-  const int db = wave % C::NDB;
-  const int dq_k0 = (wave / C::NDB) * C::DQ_KEYS;
 
   load_q(i0);
-  store_q();
+  store_q(i0, 0);
   wait_vmem_all();
   __syncthreads();
 
   for (int it = 0; it < nsteps; ++it) {
     const int i = i0 + it;
+    const int cur = it & 1;
     const int q0 = i * BRB;
     if (it + 1 < nsteps) load_q(i + 1);
+    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N);
 
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qb0 = q0 + 32 * qb;  // first query of this 32-query block
-      const bool idle = (CAUSAL && qb0 + 31 < kw0) || kw0 >= N;
-      if (idle) {
-        // every score of this wave's keys is masked here: dS = 0 for its columns
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          dss[m * DSS + 32 * wave + l32] = (__bf16)0.f;
-        }
-        continue;
-      }
-      f32x16 s = f32x16{}, dp = f32x16{};
+    // first product: S = Q K^T (P-wave) or dP = dO V^T (dS-wave);
+    // M = 32 queries, N = this block's 32 keys; lane = one key, 16 queries
+    f32x16 sd = f32x16{};
+    {
+      const __bf16* a_tile = pwave ? qs[cur] : dos[cur];
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const int c = 2 * st + hh;
-        const int qr = 32 * qb + l32;
-        const bf16x8 aq = ld_lds16(&qs[qr * D + ((c ^ (qr & (CH - 1))) * 8)]);
-        s = mfma32(aq, kf[st], s);
-        const bf16x8 ao = ld_lds16(&dos[qr * D + ((c ^ (qr & (CH - 1))) * 8)]);
-        dp = mfma32(ao, vf[st], dp);
-      }
+      for (int st = 0; st < D / 16; ++st)
+        sd = mfma32(ld_lds16(&a_tile[tile_off<D>(l32, 16 * st + 8 * hh)]), frag[st], sd);
+      // P-waves: dQ of the previous step (its dS^T was published by the last barrier)
+      if (pwave && it > 0) dq_step(q0 - BRB, cur ^ 1);
       __builtin_amdgcn_s_setprio(0);
-      const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (kw0 + 32 > N);
-      u32x4 pt[2], dst[2];
+    }
+
+    u32x4 opnd[2];  // P^T (P-wave) or dS^T (dS-wave) as A operands, 2 k-steps
+    if (pwave) {
+      // P = exp2(c S - LSE2); hand P (float32, lane-major) to the dS-wave
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        // queries 8g + 4hh + 0..3 of this block: two (LSE2, D) pairs per 16 bytes
-        const int m0 = 32 * qb + 8 * g + 4 * hh;
-        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[m0]);
-        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[m0 + 2]);
+        const int m0 = 8 * g + 4 * hh;
+        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
+        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
         const float l2v[4] = {st01[0], st01[2], st23[0], st23[2]};
-        const float dvv[4] = {st01[1], st01[3], st23[1], st23[3]};
-        float p[4], ds[4];
+        f32x4 p;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pv = fast_exp2(__builtin_fmaf(s[r], c_log2, -l2v[e]));
+          float pv = fast_exp2(__builtin_fmaf(sd[4 * g + e], c_log2, -l2v[e]));
           if (need_mask) {
-            const int q = qb0 + 8 * g + 4 * hh + e;
+            const int q = q0 + m0 + e;
             if (key >= N || (CAUSAL && key > q)) pv = 0.f;
           }
           p[e] = pv;
-          ds[e] = pv * (dp[r] - dvv[e]);
         }
+        ps[kblk][g][lane] = p;
         // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
-        pt[g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
-        pt[g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
-        const uint32_t d01 = pack_bf16(ds[0], ds[1]);
-        const uint32_t d23 = pack_bf16(ds[2], ds[3]);
-        dst[g >> 1][2 * (g & 1)] = d01;
-        dst[g >> 1][2 * (g & 1) + 1] = d23;
-        __bf16* col = &dss[m0 * DSS + 32 * wave + l32];
-        col[0] = __builtin_bit_cast(bf16x2, d01)[0];
-        col[DSS] = __builtin_bit_cast(bf16x2, d01)[1];
-        col[2 * DSS] = __builtin_bit_cast(bf16x2, d23)[0];
-        col[3 * DSS] = __builtin_bit_cast(bf16x2, d23)[1];
+        opnd[g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
+        opnd[g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
       }
-      // dV += P^T dO, dK += dS^T Q   (M = keys, N = d, k = queries of this block)
+    }
+    __syncthreads();  // P handed over
+    if (!pwave) {
+      // dS = P (dP - D); dS^T into LDS for the dQ products
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m0 = 8 * g + 4 * hh;
+        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
+        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
+        const float dvv[4] = {st01[1], st01[3], st23[1], st23[3]};
+        const f32x4 p = ps[kblk][g][lane];
+        float ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[4 * g + e] - dvv[e]);
+        const u32x2 d4 = {pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
+        opnd[g >> 1][2 * (g & 1)] = d4[0];
+        opnd[g >> 1][2 * (g & 1) + 1] = d4[1];
+        st_lds8(&dsts[cur][dst_off(kw0 - k0 + l32, m0)], d4);  // dS^T[key][m0..m0+3]
+      }
+    }
+
+    // second product: dV += P^T dO (P-wave) or dK += dS^T Q (dS-wave);
+    // M = keys, N = d, k = queries; the B operand is read transposed from the
+    // row-major tile, rows in the A operand's slot order
+    {
+      const __bf16* b_tile = pwave ? dos[cur] : qs[cur];
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        const int r_lo = 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
+        const int r_hi = r_lo + 8;                // slots 8hh + 4..7
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
-          const int qoff = 32 * qb + 16 * t + 8 * hh;
-          const bf16x8 bo = ld_lds16(&dotr[(32 * b + l32) * QTS + qoff]);
-          dv[b] = mfma32(as_bf16x8(pt[t]), bo, dv[b]);
-          const bf16x8 bq = ld_lds16(&qtr[(32 * b + l32) * QTS + qoff]);
-          dk[b] = mfma32(as_bf16x8(dst[t]), bq, dk[b]);
-        }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    __syncthreads();
-
-    // dQ[q0.., 32 db ..] += dS[:, keys] K[keys, 32 db ..]   (M = queries, N = d)
-    {
-      f32x16 acc[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < C::DQ_KEYS / 16; ++t) {
-        const int kk = dq_k0 + 16 * t + 8 * hh;
-        const bf16x8 b = ld_lds16(&kt[(32 * db + l32) * KTS + kk]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const bf16x8 a = ld_lds16(&dss[(32 * qb + l32) * DSS + kk]);
-          acc[qb] = mfma32(a, b, acc[qb]);
+          const int col = 32 * b + tr_col;
+          const bf16x8 bb = cat8(ld_lds_tr(&b_tile[tile_off<D>(r_lo, col)]),
+                                 ld_lds_tr(&b_tile[tile_off<D>(r_hi, col)]));
+          acc_kd[b] = mfma32(as_bf16x8(opnd[t]), bb, acc_kd[b]);
         }
       }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          buf_atomic_add(rdQ, ((uint32_t)q * D + 32 * db + l32) * 4u, acc[qb][r]);
-        }
+      __builtin_amdgcn_s_setprio(0);
     }
-    if (it + 1 < nsteps) store_q();
+    if (it + 1 < nsteps) store_q(i + 1, cur ^ 1);
     __syncthreads();
   }
+  // dQ of the last step
+  if (pwave) dq_step((i0 + nsteps - 1) * BRB, (nsteps - 1) & 1);
 
-  // ---- epilogue: dK = scale * dK_acc, dV = dV_acc, bf16 ----------------------
+  // ---- epilogue: dV = dV_acc (P-waves), dK = scale * dK_acc (dS-waves), bf16 --
+  __bf16* out = pwave ? dV : dK;
+  const float osc = pwave ? 1.f : scale;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kk < N) {
-        const size_t off = head + (size_t)kk * D + 32 * b + l32;
-        dK[off] = (__bf16)(dk[b][r] * scale);
-        dV[off] = (__bf16)dv[b][r];
-      }
+      if (kk < N) out[head + (size_t)kk * D + 32 * b + l32] = (__bf16)(acc_kd[b][r] * osc);
     }
 }
 
@@ -357,13 +356,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ a
   reinterpret_cast<u32x4*>(dQ)[i] = w;
 }
 
-#ifndef FA_BWD_BRB
-#define FA_BWD_BRB 64
-#endif
-
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
-  using C = BwdCfg<D, FA_BWD_BRB>;
+  using C = BwdCfg<D>;
   const long long rows = (long long)a.B * a.H * a.N;
   f32x2* rowstat = reinterpret_cast<f32x2*>(a.rowstat);
   {
@@ -377,7 +372,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     const int nkb = (a.N + C::BCB - 1) / C::BCB;
     const long long total = (long long)nkb * a.B * a.H;
     const hipError_t e = launch_kernel(
-        bwd_kernel<D, FA_BWD_BRB, CAUSAL>, dim3((unsigned)total), dim3(256), a.stream,
+        bwd_kernel<D, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
         (const f32x2*)rowstat, a.dq_acc, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H,
         a.softmax_scale * kLog2e, a.softmax_scale);

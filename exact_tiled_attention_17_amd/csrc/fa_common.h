@@ -92,6 +92,20 @@ __device__ __forceinline__ void st_lds8(__bf16* p, u32x2 v) {
   *reinterpret_cast<u32x2*>(p) = v;
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane 16g+i reads 4 bf16 at its own address; lane 16g+t then receives element
+// (t & 3) of the reads of lanes 16g + (t >> 2) + 4e, for e = 0..3. So to give
+// lane l the values X[row(e)][col0 + l % 16] of a row-major tile X, lane 16g+i
+// passes the address of X[row(i >> 2)][col0 + 4 (i & 3)].
+__device__ __forceinline__ bf16x4 ld_lds_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Interleave four rows of eight bf16 (one 16-byte chunk each, rows r0..r3)
 // into eight 4-element columns: column e = (r0[e], r1[e], r2[e], r3[e]).
 // Used to write a transposed tile into LDS with 8-byte stores.
