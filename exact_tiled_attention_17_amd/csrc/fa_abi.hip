@@ -65,15 +65,12 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
   if (LSE == nullptr || !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const size_t rows = (size_t)B * H * N;
   void* scratch = nullptr;
   const hipError_t m = hipMallocAsync(&scratch, fa::bwd_scratch_bytes(B, H, N, d), s);
   if (m != hipSuccess || scratch == nullptr)
     return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
-  float* dq_acc = static_cast<float*>(scratch);
-  float* rowstat = dq_acc + rows * (size_t)d;
   fa::BwdArgs a{Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal != 0, softmax_scale, s,
-                dq_acc, rowstat};
+                static_cast<float*>(scratch)};
   const hipError_t e = fa::launch_bwd(a);
   const hipError_t f = hipFreeAsync(scratch, s);
   return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);

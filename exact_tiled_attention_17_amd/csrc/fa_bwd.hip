@@ -2,29 +2,31 @@
 //
 // The probabilities are recomputed from the stored log-sum-exp rather than
 // kept ("GPU Performance Optimization Batch 1 - Design Spec", Item 3, Design,
-// backward file), and dQ is gathered with atomic updates ("RTX Flash Attention
-// Implementation COMPLETE", CUDA Kernel Design, backward kernel: gradient
-// recomputation and atomic memory operations). Three launches on one stream:
+// backward file). Three launches on one stream:
 //
 //  1. bwd_pre_kernel: per query row, D_i = dO_i . O_i (float32) and the LSE in
-//     base 2; zeroes the float32 dQ accumulator.
-//  2. bwd_kernel: one workgroup per (batch, head, block of 128 keys); each
+//     base 2.
+//  2. bwd_dkdv_kernel: one workgroup per (batch, head, block of 128 keys); each
 //     32-key block has a P-wave (dV) and a dS-wave (dK) on one SIMD, holding
 //     float32 accumulators for the whole sweep over query tiles of 32 rows.
-//     The K block and the Q, dO tiles sit row-major in LDS; operands that need
-//     them transposed use gfx950's transposing LDS read instead of a second,
-//     transposed copy. Per query tile, on 32x32x16 bf16 matrix cores:
+//     The Q, dO tiles sit row-major in LDS; operands that need them transposed
+//     use gfx950's transposing LDS read instead of a second, transposed copy.
+//     Per query tile, on 32x32x16 bf16 matrix cores:
 //        S = Q K^T, dP = dO V^T        (lane = one key, 16 queries)
 //        P = exp2(c S - LSE2), dS = P (dP - D)
 //        dV += P^T dO, dK += dS^T Q    (P^T, dS^T straight from registers)
-//        dQ += dS K                    (dS^T through LDS, float32 atomics)
-//     dQ of a step runs during the next step's S/dP products (query-side
-//     tiles double-buffered), so each step has one barrier.
 //     Causal: query tiles that see none of the block's keys are skipped.
-//  3. bwd_dq_kernel: dQ = bf16(scale * dQ_acc).
+//  3. bwd_dq_kernel: one workgroup per (batch, head, query tile), sweeping key
+//     tiles like the forward: S and dP are recomputed and dQ += dS K is summed
+//     in registers, so dQ needs no atomics and no float32 scratch.
 //
-// Global reads and the dQ atomics go through buffer resources, so rows past
-// the end of the sequence read as zeros / are dropped without branches.
+// The pages' backward gathers dQ with atomic updates ("RTX Flash Attention
+// Implementation COMPLETE", CUDA Kernel Design, backward kernel); on MI355X the
+// float32 atomics cost more than recomputing S and dP in a second pass, so
+// this backward recomputes instead.
+//
+// Global reads go through buffer resources, so rows past the end of the
+// sequence read as zeros without branches.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -32,13 +34,12 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// 1. Row statistics and dQ accumulator reset
+// 1. Row statistics
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
                                                      const __bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE,
-                                                     float* __restrict__ dq_acc,
                                                      f32x2* __restrict__ rowstat, long long rows) {
   constexpr int CH = D / 8;  // lanes per row
   const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -53,9 +54,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
       acc += __uint_as_float(a[m] << 16) * __uint_as_float(b[m] << 16);
       acc += __uint_as_float(a[m] & 0xFFFF0000u) * __uint_as_float(b[m] & 0xFFFF0000u);
     }
-    f32x4* z = reinterpret_cast<f32x4*>(dq_acc + row * D + 8 * c);
-    z[0] = f32x4{};
-    z[1] = f32x4{};
   }
 #pragma unroll
   for (int off = CH / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, CH);
@@ -73,12 +71,8 @@ struct BwdCfg {
   static constexpr int BCB = 32 * KBLK;     // keys per workgroup
   static constexpr int BRB = 32;            // queries per step
   static constexpr int CH = D / 8;          // 16-byte chunks per row
-  static constexpr int NDB = D / 32;        // 32-wide column blocks of d
-  static constexpr int KSPLIT = KBLK / NDB;       // P-waves sharing one dQ column block
-  static constexpr int DQ_KEYS = BCB / KSPLIT;    // keys each P-wave sums for dQ
   static constexpr int TPT = 2 * BRB * CH / THREADS;  // Q/dO tile chunks per thread
-  static constexpr int KPT = BCB * CH / THREADS;      // K-block chunks per thread
-  static_assert(TPT >= 1 && KPT >= 1 && KSPLIT >= 1, "work split");
+  static_assert(TPT >= 1, "work split");
 };
 
 // Row-major tiles of d-wide rows keep 16-byte chunk c of row r at chunk
@@ -94,32 +88,22 @@ template <int D>
 __device__ __forceinline__ int tile_off(int r, int col) {  // element offset of (r, col), col % 4 == 0
   return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 4);
 }
-// dS^T tile: [128 keys][32 queries], 8-byte units u of row r at u ^ ((r >> 2) & 7):
-// conflict-free both for a wave's 8-byte column writes and for transposing reads.
-__device__ __forceinline__ int dst_off(int r, int col) {
-  return r * 32 + ((((col >> 2) ^ (r >> 2)) & 7) << 2);
-}
-
 // Each 32-key block of the workgroup is served by two waves on one SIMD:
-//   P-wave:  S = Q K^T, P = exp2(c S - LSE2), dV += P^T dO, and (one step
-//            late) dQ += dS K for its column block, with float32 atomics;
+//   P-wave:  S = Q K^T, P = exp2(c S - LSE2), dV += P^T dO;
 //   dS-wave: dP = dO V^T, dS = P (dP - D) with P from its partner through
-//            LDS, dK += dS^T Q, and dS^T into LDS for the dQ products.
+//            LDS, dK += dS^T Q.
 // Splitting the dK and dV accumulators keeps each wave under 256 registers,
 // so two waves share a SIMD and one's softmax overlaps the other's products.
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                const f32x2* __restrict__ rowstat, float* __restrict__ dq_acc,
-                __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH,
-                float c_log2, float scale) {
+void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                     const f32x2* __restrict__ rowstat, __bf16* __restrict__ dK,
+                     __bf16* __restrict__ dV, int N, int BH, float c_log2, float scale) {
   using C = BwdCfg<D>;
   constexpr int BCB = C::BCB, BRB = C::BRB, CH = C::CH;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[BCB * D];         // K block, row-major
   __shared__ __attribute__((aligned(16))) __bf16 qs[2][BRB * D];      // Q tiles
   __shared__ __attribute__((aligned(16))) __bf16 dos[2][BRB * D];     // dO tiles
-  __shared__ __attribute__((aligned(16))) __bf16 dsts[2][BCB * BRB];  // dS^T tiles
   __shared__ __attribute__((aligned(16))) f32x4 ps[C::KBLK][4][64];   // P, lane-major
   __shared__ __attribute__((aligned(16))) f32x2 rs[2][BRB];           // (LSE2, D) per query
 
@@ -145,7 +129,6 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rK = make_rsrc(K + head, head_bytes);
   const auto rV = make_rsrc(V + head, head_bytes);
   const auto rdO = make_rsrc(dO + head, head_bytes);
-  const auto rdQ = make_rsrc(dq_acc + head, head_bytes * 2u);
   const auto rRS = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 8u);
 
   const int k0 = kb * BCB;
@@ -159,13 +142,6 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
       frag[s] = as_bf16x8(buf_load16(rF, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
-  }
-  // K block into LDS (row-major, swizzled) for the dQ products
-#pragma unroll
-  for (int r = 0; r < C::KPT; ++r) {
-    const int i = tid + r * C::THREADS;
-    const int kr = i / CH, c = i % CH;
-    st_lds16(&ks[tile_off<D>(kr, 8 * c)], buf_load16(rK, (uint32_t)(k0 + kr) * (D * 2) + c * 16));
   }
 
   // Q / dO tile loaders: P-waves load Q, dS-waves dO
@@ -194,30 +170,6 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // rows past the end get LSE2 = +inf and D = 0, so their P and dS are 0
     if (wave == C::NW - 1 && lane < BRB)
       rs[buf][lane] = i * BRB + lane < N ? rstg : f32x2{INFINITY, 0.f};
-  };
-
-  // dQ[q0.., 32 db ..] += dS K for the step whose dS^T sits in dsts[buf]
-  // (P-waves; M = queries, N = d, k = keys in natural order; both operands
-  // read transposed: dS from dS^T, K from the K block)
-  const int db = kblk % C::NDB;
-  const int dq_k0 = (kblk / C::NDB) * C::DQ_KEYS;
-  auto dq_step = [&](int q0, int buf) {
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int t = 0; t < C::DQ_KEYS / 16; ++t) {
-      const int r_lo = dq_k0 + 16 * t + 8 * hh + tr_e;
-      const int r_hi = r_lo + 4;
-      const bf16x8 a = cat8(ld_lds_tr(&dsts[buf][dst_off(r_lo, tr_col)]),
-                            ld_lds_tr(&dsts[buf][dst_off(r_hi, tr_col)]));
-      const bf16x8 b = cat8(ld_lds_tr(&ks[tile_off<D>(r_lo, 32 * db + tr_col)]),
-                            ld_lds_tr(&ks[tile_off<D>(r_hi, 32 * db + tr_col)]));
-      acc = mfma32(a, b, acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      buf_atomic_add(rdQ, ((uint32_t)q * D + 32 * db + l32) * 4u, acc[r]);
-    }
   };
 
   // this wave's accumulator: dV (P-wave) or dK (dS-wave), M = keys, N = d
@@ -250,8 +202,6 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int st = 0; st < D / 16; ++st)
         sd = mfma32(ld_lds16(&a_tile[tile_off<D>(l32, 16 * st + 8 * hh)]), frag[st], sd);
-      // P-waves: dQ of the previous step (its dS^T was published by the last barrier)
-      if (pwave && it > 0) dq_step(q0 - BRB, cur ^ 1);
       __builtin_amdgcn_s_setprio(0);
     }
 
@@ -282,7 +232,7 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     __syncthreads();  // P handed over
     if (!pwave) {
-      // dS = P (dP - D); dS^T into LDS for the dQ products
+      // dS = P (dP - D)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int m0 = 8 * g + 4 * hh;
@@ -296,7 +246,6 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const u32x2 d4 = {pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
         opnd[g >> 1][2 * (g & 1)] = d4[0];
         opnd[g >> 1][2 * (g & 1) + 1] = d4[1];
-        st_lds8(&dsts[cur][dst_off(kw0 - k0 + l32, m0)], d4);  // dS^T[key][m0..m0+3]
       }
     }
 
@@ -323,8 +272,6 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (it + 1 < nsteps) store_q(i + 1, cur ^ 1);
     __syncthreads();
   }
-  // dQ of the last step
-  if (pwave) dq_step((i0 + nsteps - 1) * BRB, (nsteps - 1) & 1);
 
   // ---- epilogue: dV = dV_acc (P-waves), dK = scale * dK_acc (dS-waves), bf16 --
   __bf16* out = pwave ? dV : dK;
@@ -339,49 +286,222 @@ void bwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = bf16(scale * dQ_acc)
+// 3. dQ kernel
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ acc,
-                                                    __bf16* __restrict__ dQ, float scale,
-                                                    long long n8) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = reinterpret_cast<const f32x4*>(acc)[2 * i];
-  const f32x4 b = reinterpret_cast<const f32x4*>(acc)[2 * i + 1];
-  u32x4 w;
-  w[0] = pack_bf16(a[0] * scale, a[1] * scale);
-  w[1] = pack_bf16(a[2] * scale, a[3] * scale);
-  w[2] = pack_bf16(b[0] * scale, b[1] * scale);
-  w[3] = pack_bf16(b[2] * scale, b[3] * scale);
-  reinterpret_cast<u32x4*>(dQ)[i] = w;
+// One workgroup per (batch, head, tile of 32*NW queries); each wave owns 32
+// query rows and sweeps the key tiles like the forward kernel does, with the
+// products transposed so that a lane owns one query:
+//   S^T = K_j Q^T, dP^T = V_j dO^T     (lane = one query, 16 keys per block)
+//   P^T = exp2(c S^T - LSE2), dS^T = P^T (dP^T - D)   (LSE2, D: the lane's own)
+//   dQ^T += K_j^T dS^T                 (dS^T straight from registers; K_j^T
+//                                       by transposing reads of the K tile)
+// and writes dQ = scale * dQ^T as bf16. No atomics: each dQ row is summed
+// over all keys inside one wave.
+template <int D, int NW>
+struct DqCfg {
+  static constexpr int BR = 32 * NW;  // query rows per workgroup
+  static constexpr int BC = 64;       // keys per K/V tile
+  static constexpr int CH = D / 8;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int LOADERS = THREADS / 2;  // half load K, half V
+  static constexpr int TPT = BC * CH / LOADERS;
+  static_assert(TPT >= 1 && BC * CH % LOADERS == 0, "loaders");
+};
+
+template <int D, int NW, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW)))
+void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                   const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                   const f32x2* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
+                   float c_log2, float scale) {
+  using C = DqCfg<D, NW>;
+  constexpr int BR = C::BR, BC = C::BC, CH = C::CH;
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BC * D];  // K tiles, row-major
+  __shared__ __attribute__((aligned(16))) __bf16 vs[2][BC * D];  // V tiles, row-major
+
+  const int nq = (N + BR - 1) / BR;
+  int bh, qt;
+  xcd_remap(blockIdx.x, nq * BH, nq, bh, qt);
+  if (CAUSAL) qt = nq - 1 - qt;  // longest rows first
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int tr_grp = lane >> 4, tr_i = lane & 15;
+  const int tr_e = tr_i >> 2;
+  const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto rQ = make_rsrc(Q + head, head_bytes);
+  const auto rK = make_rsrc(K + head, head_bytes);
+  const auto rV = make_rsrc(V + head, head_bytes);
+  const auto rdO = make_rsrc(dO + head, head_bytes);
+  const auto rRS = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 8u);
+
+  const int q0 = qt * BR;
+  const int wrow0 = q0 + 32 * wave;
+  const int row = wrow0 + l32;
+  const int nkv_all = (N + BC - 1) / BC;
+  const int last_row_wg = min(q0 + BR, N) - 1;
+  const int nkv = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;
+  const bool wave_active = wrow0 < N;
+  const int jw_last = CAUSAL ? min(wrow0 + 31, N - 1) / BC : nkv - 1;
+
+  // Q^T and dO^T operands (rows past N read as zeros) and the row statistics
+  bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const uint32_t off = (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2;
+    qf[s] = as_bf16x8(buf_load16(rQ, off));
+    of[s] = as_bf16x8(buf_load16(rdO, off));
+  }
+  const f32x2 rst = __builtin_bit_cast(
+      f32x2, __builtin_amdgcn_raw_buffer_load_b64(rRS, (uint32_t)row * 8u, 0, 0));
+  const float neg_l2 = -rst[0], dval = rst[1];
+
+  // K / V tile loaders (wave-uniform roles), row-major swizzled tiles
+  const bool k_loader = wave < NW / 2;
+  const int lt = tid % C::LOADERS;
+  const auto rT = k_loader ? rK : rV;
+  u32x4 stg[C::TPT];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < C::TPT; ++r) {
+      const int i = lt + r * C::LOADERS;
+      stg[r] = buf_load16(rT, (uint32_t)(j * BC + i / CH) * (D * 2) + (i % CH) * 16);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __bf16* t = k_loader ? ks[buf] : vs[buf];
+#pragma unroll
+    for (int r = 0; r < C::TPT; ++r) {
+      const int i = lt + r * C::LOADERS;
+      st_lds16(&t[tile_off<D>(i / CH, 8 * (i % CH))], stg[r]);
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
+
+  load_tile(0);
+  store_tile(0);
+  wait_vmem_all();
+  __syncthreads();
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkv) load_tile(j + 1);
+
+    if (wave_active && j <= jw_last) {
+      // S^T = K_j Q^T and dP^T = V_j dO^T: two 32-key blocks each
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb) {
+          const int off = tile_off<D>(32 * kb + l32, 16 * st + 8 * hh);
+          s[kb] = mfma32(ld_lds16(&ks[buf][off]), qf[st], s[kb]);
+          dp[kb] = mfma32(ld_lds16(&vs[buf][off]), of[st], dp[kb]);
+        }
+      __builtin_amdgcn_s_setprio(0);
+
+      const int kv0 = j * BC;
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
+      u32x4 dsf[BC / 16];  // dS^T as B operands, 4 k-steps of 16 keys
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float d2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float p = fast_exp2(__builtin_fmaf(s[kb][r + u], c_log2, neg_l2));
+            if (need_mask) {
+              const int kk = kv0 + 32 * kb + 8 * ((r + u) >> 2) + 4 * hh + ((r + u) & 3);
+              if (kk >= N || (CAUSAL && kk > row)) p = 0.f;
+            }
+            d2[u] = p * (dp[kb][r + u] - dval);
+          }
+          dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16(d2[0], d2[1]);
+        }
+
+      // dQ^T += K_j^T dS^T   (M = d, N = queries, k = keys in the dS^T slot order)
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int t = 0; t < BC / 16; ++t) {
+        const int r_lo = 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
+        const int r_hi = r_lo + 8;                // slots 8hh + 4..7
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          const int col = 32 * b + tr_col;
+          const bf16x8 a = cat8(ld_lds_tr(&ks[buf][tile_off<D>(r_lo, col)]),
+                                ld_lds_tr(&ks[buf][tile_off<D>(r_hi, col)]));
+          acc[b] = mfma32(a, as_bf16x8(dsf[t]), acc[b]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+
+    if (j + 1 < nkv) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dQ = scale * dQ^T, bf16 ---------------------------------------
+  if (!wave_active || row >= N) return;
+  __bf16* Drow = dQ + head + (size_t)row * D;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16(acc[b][4 * g] * scale, acc[b][4 * g + 1] * scale);
+      w[1] = pack_bf16(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
+      st_global8(Drow + 32 * b + 8 * g + 4 * hh, w);
+    }
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   using C = BwdCfg<D>;
+  constexpr int DQ_NW = D == 128 ? 8 : 4;
+  using Cq = DqCfg<D, DQ_NW>;
   const long long rows = (long long)a.B * a.H * a.N;
   f32x2* rowstat = reinterpret_cast<f32x2*>(a.rowstat);
+  const float c_log2 = a.softmax_scale * kLog2e;
   {
     const long long threads = rows * (D / 8);
     const hipError_t e = launch_kernel(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)),
                                        dim3(256), a.stream, (const __bf16*)a.O, (const __bf16*)a.dO,
-                                       a.LSE, a.dq_acc, rowstat, rows);
+                                       a.LSE, rowstat, rows);
     if (e != hipSuccess) return e;
   }
   {
     const int nkb = (a.N + C::BCB - 1) / C::BCB;
     const long long total = (long long)nkb * a.B * a.H;
     const hipError_t e = launch_kernel(
-        bwd_kernel<D, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+        bwd_dkdv_kernel<D, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
-        (const f32x2*)rowstat, a.dq_acc, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H,
-        a.softmax_scale * kLog2e, a.softmax_scale);
+        (const f32x2*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, c_log2,
+        a.softmax_scale);
     if (e != hipSuccess) return e;
   }
   {
-    const long long n8 = rows * D / 8;
-    return launch_kernel(bwd_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), a.stream,
-                         (const float*)a.dq_acc, (__bf16*)a.dQ, a.softmax_scale, n8);
+    const int nq = (a.N + Cq::BR - 1) / Cq::BR;
+    const long long total = (long long)nq * a.B * a.H;
+    return launch_kernel(bwd_dq_kernel<D, DQ_NW, CAUSAL>, dim3((unsigned)total),
+                         dim3(Cq::THREADS), a.stream, (const __bf16*)a.Q, (const __bf16*)a.K,
+                         (const __bf16*)a.V, (const __bf16*)a.dO, (const f32x2*)rowstat,
+                         (__bf16*)a.dQ, a.N, a.B * a.H, c_log2, a.softmax_scale);
   }
 }
 

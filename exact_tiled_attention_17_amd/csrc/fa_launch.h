@@ -32,7 +32,6 @@ struct BwdArgs {
   bool causal;
   float softmax_scale;
   hipStream_t stream;
-  float* dq_acc;  // [B,H,N,d] float32 scratch
   float* rowstat; // [B,H,N] x 2 float32 scratch: (LSE in base 2, D = dO . O)
 };
 
@@ -55,8 +54,8 @@ hipError_t launch_bwd(const BwdArgs& a);
 
 // Scratch bytes fa_bwd needs for a problem of this size.
 inline size_t bwd_scratch_bytes(int B, int H, int N, int d) {
-  const size_t rows = (size_t)B * H * N;
-  return rows * (size_t)d * 4 + rows * 8;
+  (void)d;
+  return (size_t)B * H * N * 8;
 }
 
 }  // namespace fa

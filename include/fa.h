@@ -84,7 +84,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *   LSE             in : [B,H,N] float32, must not be NULL
  *   dQ, dK, dV      out: [B,H,N,d] bf16
  *
- * Needs float32 scratch of 4*B*H*N*(d+2) bytes, taken stream-ordered with
+ * Needs float32 scratch of 8*B*H*N bytes, taken stream-ordered with
  * hipMallocAsync on `stream` and released with hipFreeAsync on the same
  * stream (no host synchronisation). Returns FA_ERR_OUT_OF_MEMORY if it cannot
  * be had.
