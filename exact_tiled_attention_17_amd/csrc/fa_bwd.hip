@@ -75,19 +75,6 @@ struct BwdCfg {
   static_assert(TPT >= 1, "work split");
 };
 
-// Row-major tiles of d-wide rows keep 16-byte chunk c of row r at chunk
-// position c ^ swz(r). For d = 128 the swizzle makes both access patterns
-// conflict-free: 16 consecutive rows at one chunk (operand rows), and 4
-// consecutive rows x 4 consecutive chunks (transposing reads).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (r >> 1) & 7;
-}
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int col) {  // element offset of (r, col), col % 4 == 0
-  return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 4);
-}
 // Each 32-key block of the workgroup is served by two waves on one SIMD:
 //   P-wave:  S = Q K^T, P = exp2(c S - LSE2), dV += P^T dO;
 //   dS-wave: dP = dO V^T, dS = P (dP - D) with P from its partner through

@@ -130,6 +130,19 @@ __device__ __forceinline__ int kperm(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// Row-major tiles of d-wide rows keep 16-byte chunk c of row r at chunk
+// position c ^ swz(r). For d = 128 the swizzle makes both access patterns
+// conflict-free: 16 consecutive rows at one chunk (operand rows), and 4
+// consecutive rows x 4 consecutive chunks (transposing reads).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {  // element offset of (r, col), col % 4 == 0
+  return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 4);
+}
 // Maps a linear workgroup id to (head, tile) so that the workgroups that land
 // on one XCD (the hardware deals ids round-robin over the 8 XCDs) cover whole
 // heads, which then share that XCD's L2; within an XCD, heads go one after the

@@ -14,12 +14,14 @@
 //    the other 16), so the row max needs one cross-lane swap, the row sum none
 //    until the end, and the rescale factor of a lane's O^T accumulators is the
 //    lane's own. P^T goes from the S^T registers straight into the B operand of
-//    the second product (no LDS round trip); V^T is stored with its keys
-//    permuted to match.
+//    the second product (no LDS round trip); the V^T operand comes from the
+//    row-major V tile through gfx950's transposing LDS read, rows taken in the
+//    key order of the P^T operand.
 //  * K/V tiles of BC = 64 keys are staged in LDS, double buffered: the global
 //    loads of tile j+1 are issued before tile j is computed and written to LDS
-//    after it, one barrier per tile. K is kept row-major with an XOR swizzle on
-//    16-byte chunks (conflict-free operand reads); V is written transposed.
+//    after it, one barrier per tile. Both tiles are row-major with an XOR
+//    swizzle on 16-byte chunks that keeps operand-row reads and transposing
+//    reads free of bank conflicts.
 //  * Causal: tiles entirely above the diagonal are never loaded; a wave skips
 //    tiles fully masked for its own rows; masks are applied only to tiles that
 //    cross the diagonal or the end of the sequence.
@@ -43,13 +45,10 @@ struct FwdCfg {
   static constexpr int BR = 32 * NW;  // query rows per workgroup
   static constexpr int BC = 64;       // keys per K/V tile
   static constexpr int CH = D / 8;    // 16-byte chunks per row
-  static constexpr int VTS = BC + 8;  // padded row length (elements) of the V^T tile
   static constexpr int THREADS = 64 * NW;
   static constexpr int LOADERS = THREADS / 2;  // half the threads load K, half V
-  static constexpr int KPT = BC * CH / LOADERS;        // K chunks per loader thread
-  static constexpr int VPT = (BC / 4) * CH / LOADERS;  // V 4-key groups per loader thread
-  static_assert(KPT >= 1 && VPT >= 1 && KPT == 4 * VPT, "loader split");
-  static_assert(BC * CH % LOADERS == 0 && (BC / 4) * CH % LOADERS == 0, "loader split");
+  static constexpr int TPT = BC * CH / LOADERS;  // 16-byte chunks per loader thread
+  static_assert(TPT >= 1 && BC * CH % LOADERS == 0, "loader split");
 };
 
 template <int D, int NW, bool CAUSAL>
@@ -58,14 +57,14 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O,
                 float* __restrict__ LSE, int N, int BH, float c_log2) {
   using C = FwdCfg<D, NW>;
-  constexpr int BR = C::BR, BC = C::BC, CH = C::CH, VTS = C::VTS;
+  constexpr int BR = C::BR, BC = C::BC, CH = C::CH;
   // Lazy rescaling: the running max used for P only moves when the true row
   // max exceeds it by more than TAU (base-2 units), so P <= 2^TAU and the
   // O^T rescale is skipped on most tiles. The result is exact either way:
   // O = sum_j 2^(c s_j - m) v_j / sum_j 2^(c s_j - m) for any common m.
   constexpr float TAU = 8.f;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) __bf16 vt[2][D * VTS];
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BC * D];  // K tiles, row-major
+  __shared__ __attribute__((aligned(16))) __bf16 vs[2][BC * D];  // V tiles, row-major
 
   const int nq = (N + BR - 1) / BR;
   int bh, qt;
@@ -77,6 +76,9 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  const int tr_grp = lane >> 4, tr_i = lane & 15;         // transposing-read addressing
+  const int tr_e = tr_i >> 2;
+  const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -99,62 +101,25 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int s = 0; s < D / 16; ++s)
     qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
 
-  // ---- K/V tile staging -----------------------------------------------------
-  // K loaders: chunk i -> (key i / CH, 16-byte chunk i % CH), rows contiguous.
-  // V loaders: group g -> (4 keys from 4 kg, chunk dc); within 16 lanes, 4 key
-  // groups x 4 chunks, so the transposed 8-byte LDS writes spread over banks
-  // while each global read still covers 64 contiguous bytes of a row.
-  const bool k_loader = wave < NW / 2;  // wave-uniform: a scalar branch
-  const int lt = k_loader ? tid : tid - C::LOADERS;
-  u32x4 stg[C::KPT];
-  auto v_group = [&](int g, int& kg, int& dc) {
-    constexpr int DCH = CH / 4;  // dc_hi range
-    const int dc_lo = g & 3, kg_lo = (g >> 2) & 3;
-    const int rest = g >> 4;
-    const int dc_hi = rest % DCH, kg_hi = rest / DCH;
-    dc = dc_hi * 4 + dc_lo;
-    kg = kg_hi * 4 + kg_lo;
-  };
-
+  // ---- K/V tile staging: waves 0..NW/2-1 load K, the rest V (wave-uniform);
+  // both tiles row-major with the chunk swizzle of tile_off ---------------------
+  const bool k_loader = wave < NW / 2;
+  const int lt = tid % C::LOADERS;
+  const auto rT = k_loader ? rK : rV;
+  u32x4 stg[C::TPT];
   auto load_tile = [&](int j) {
-    const int kv0 = j * BC;
-    if (k_loader) {
 #pragma unroll
-      for (int r = 0; r < C::KPT; ++r) {
-        const int i = lt + r * C::LOADERS;
-        const int key = i / CH, c = i % CH;
-        stg[r] = buf_load16(rK, (uint32_t)(kv0 + key) * (D * 2) + c * 16);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < C::VPT; ++r) {
-        int kg, dc;
-        v_group(lt + r * C::LOADERS, kg, dc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          stg[4 * r + i] = buf_load16(rV, (uint32_t)(kv0 + 4 * kg + i) * (D * 2) + dc * 16);
-      }
+    for (int r = 0; r < C::TPT; ++r) {
+      const int i = lt + r * C::LOADERS;
+      stg[r] = buf_load16(rT, (uint32_t)(j * BC + i / CH) * (D * 2) + (i % CH) * 16);
     }
   };
   auto store_tile = [&](int buf) {
-    if (k_loader) {
+    __bf16* t = k_loader ? ks[buf] : vs[buf];
 #pragma unroll
-      for (int r = 0; r < C::KPT; ++r) {
-        const int i = lt + r * C::LOADERS;
-        const int key = i / CH, c = i % CH;
-        st_lds16(&ks[buf][key * D + ((c ^ (key & (CH - 1))) * 8)], stg[r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < C::VPT; ++r) {
-        int kg, dc;
-        v_group(lt + r * C::LOADERS, kg, dc);
-        u32x2 col[8];
-        transpose4x8(stg[4 * r], stg[4 * r + 1], stg[4 * r + 2], stg[4 * r + 3], col);
-        const int pos = kperm(4 * kg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st_lds8(&vt[buf][(8 * dc + e) * VTS + pos], col[e]);
-      }
+    for (int r = 0; r < C::TPT; ++r) {
+      const int i = lt + r * C::LOADERS;
+      st_lds16(&t[tile_off<D>(i / CH, 8 * (i % CH))], stg[r]);
     }
   };
 
@@ -185,9 +150,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int st = 0; st < D / 16; ++st)
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb) {
-          const int key = 32 * kb + l32;
-          const int c = 2 * st + hh;
-          const bf16x8 a = ld_lds16(&ks[buf][key * D + ((c ^ (key & (CH - 1))) * 8)]);
+          const bf16x8 a = ld_lds16(&ks[buf][tile_off<D>(32 * kb + l32, 16 * st + 8 * hh)]);
           s[kb] = mfma32(a, qf[st], s[kb]);
         }
       __builtin_amdgcn_s_setprio(0);
@@ -236,15 +199,20 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           }
       l_run += lsum;
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T; V^T by transposing reads, keys in the P^T slot order
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < BC / 16; ++t)
+      for (int t = 0; t < BC / 16; ++t) {
+        const int r_lo = 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
+        const int r_hi = r_lo + 8;                // slots 8hh + 4..7
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
-          const bf16x8 a = ld_lds16(&vt[buf][(32 * b + l32) * VTS + 16 * t + 8 * hh]);
+          const int col = 32 * b + tr_col;
+          const bf16x8 a = cat8(ld_lds_tr(&vs[buf][tile_off<D>(r_lo, col)]),
+                                ld_lds_tr(&vs[buf][tile_off<D>(r_hi, col)]));
           o[b] = mfma32(a, as_bf16x8(pf[t]), o[b]);
         }
+      }
       __builtin_amdgcn_s_setprio(0);
     }
 
