@@ -8,7 +8,7 @@
 //     base 2.
 //  2. bwd_dkdv_kernel: one workgroup per (batch, head, block of 128 keys); each
 //     32-key block has a P-wave (dV) and a dS-wave (dK) on one SIMD, holding
-//     float32 accumulators for the whole sweep over query tiles of 32 rows.
+//     float32 accumulators for the whole sweep over query tiles of 64 rows.
 //     The Q, dO tiles sit row-major in LDS; operands that need them transposed
 //     use gfx950's transposing LDS read instead of a second, transposed copy.
 //     Per query tile, on 32x32x16 bf16 matrix cores:
@@ -69,7 +69,8 @@ struct BwdCfg {
   static constexpr int NW = 2 * KBLK;       // a P-wave and a dS-wave per key block
   static constexpr int THREADS = 64 * NW;
   static constexpr int BCB = 32 * KBLK;     // keys per workgroup
-  static constexpr int BRB = 32;            // queries per step
+  static constexpr int QB = 2;              // 32-query blocks per step
+  static constexpr int BRB = 32 * QB;       // queries per step
   static constexpr int CH = D / 8;          // 16-byte chunks per row
   static constexpr int TPT = 2 * BRB * CH / THREADS;  // Q/dO tile chunks per thread
   static_assert(TPT >= 1, "work split");
@@ -88,10 +89,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const f32x2* __restrict__ rowstat, __bf16* __restrict__ dK,
                      __bf16* __restrict__ dV, int N, int BH, float c_log2, float scale) {
   using C = BwdCfg<D>;
-  constexpr int BCB = C::BCB, BRB = C::BRB, CH = C::CH;
-  __shared__ __attribute__((aligned(16))) __bf16 qs[2][BRB * D];      // Q tiles
-  __shared__ __attribute__((aligned(16))) __bf16 dos[2][BRB * D];     // dO tiles
-  __shared__ __attribute__((aligned(16))) f32x4 ps[C::KBLK][4][64];   // P, lane-major
+  constexpr int BCB = C::BCB, BRB = C::BRB, QB = C::QB, CH = C::CH;
+  static_assert(BRB <= 64, "one row statistic per lane of one wave");
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2][BRB * D];         // Q tiles
+  __shared__ __attribute__((aligned(16))) __bf16 dos[2][BRB * D];        // dO tiles
+  __shared__ __attribute__((aligned(16))) f32x4 ps[C::KBLK][4 * QB][64];  // P, lane-major
   __shared__ __attribute__((aligned(16))) f32x2 rs[2][BRB];           // (LSE2, D) per query
 
   const int nkb = (N + BCB - 1) / BCB;
@@ -178,62 +180,72 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int cur = it & 1;
     const int q0 = i * BRB;
     if (it + 1 < nsteps) load_q(i + 1);
-    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N);
-
-    // first product: S = Q K^T (P-wave) or dP = dO V^T (dS-wave);
-    // M = 32 queries, N = this block's 32 keys; lane = one key, 16 queries
-    f32x16 sd = f32x16{};
+    // first product: S = Q K^T (P-wave) or dP = dO V^T (dS-wave), one per
+    // 32-query block; M = 32 queries, N = this block's 32 keys; lane = one
+    // key, 16 queries
+    f32x16 sd[QB];
     {
       const __bf16* a_tile = pwave ? qs[cur] : dos[cur];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int st = 0; st < D / 16; ++st)
-        sd = mfma32(ld_lds16(&a_tile[tile_off<D>(l32, 16 * st + 8 * hh)]), frag[st], sd);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sd[qb] = mfma32(ld_lds16(&a_tile[tile_off<D>(32 * qb + l32, 16 * st + 8 * hh)]),
+                          frag[st], sd[qb]);
       __builtin_amdgcn_s_setprio(0);
     }
 
-    u32x4 opnd[2];  // P^T (P-wave) or dS^T (dS-wave) as A operands, 2 k-steps
+    u32x4 opnd[QB][2];  // P^T (P-wave) or dS^T (dS-wave) as A operands, 2 k-steps each
     if (pwave) {
       // P = exp2(c S - LSE2); hand P (float32, lane-major) to the dS-wave
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m0 = 8 * g + 4 * hh;
-        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
-        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
-        const float l2v[4] = {st01[0], st01[2], st23[0], st23[2]};
-        f32x4 p;
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qb0 = q0 + 32 * qb;
+        const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (kw0 + 32 > N);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv = fast_exp2(__builtin_fmaf(sd[4 * g + e], c_log2, -l2v[e]));
-          if (need_mask) {
-            const int q = q0 + m0 + e;
-            if (key >= N || (CAUSAL && key > q)) pv = 0.f;
+        for (int g = 0; g < 4; ++g) {
+          const int m0 = 32 * qb + 8 * g + 4 * hh;
+          const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
+          const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
+          const float l2v[4] = {st01[0], st01[2], st23[0], st23[2]};
+          f32x4 p;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l2v[e]));
+            if (need_mask) {
+              const int q = q0 + m0 + e;
+              if (key >= N || (CAUSAL && key > q)) pv = 0.f;
+            }
+            p[e] = pv;
           }
-          p[e] = pv;
+          ps[kblk][4 * qb + g][lane] = p;
+          // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
+          opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
+          opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
         }
-        ps[kblk][g][lane] = p;
-        // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
-        opnd[g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
-        opnd[g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
       }
     }
     __syncthreads();  // P handed over
     if (!pwave) {
       // dS = P (dP - D)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m0 = 8 * g + 4 * hh;
-        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
-        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
-        const float dvv[4] = {st01[1], st01[3], st23[1], st23[3]};
-        const f32x4 p = ps[kblk][g][lane];
-        float ds[4];
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[4 * g + e] - dvv[e]);
-        const u32x2 d4 = {pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
-        opnd[g >> 1][2 * (g & 1)] = d4[0];
-        opnd[g >> 1][2 * (g & 1) + 1] = d4[1];
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int m0 = 32 * qb + 8 * g + 4 * hh;
+          const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
+          const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
+          const float dvv[4] = {st01[1], st01[3], st23[1], st23[3]};
+          const f32x4 p = ps[kblk][4 * qb + g][lane];
+          float ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[qb][4 * g + e] - dvv[e]);
+          opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(ds[0], ds[1]);
+          opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(ds[2], ds[3]);
+        }
     }
 
     // second product: dV += P^T dO (P-wave) or dK += dS^T Q (dS-wave);
@@ -243,17 +255,19 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const __bf16* b_tile = pwave ? dos[cur] : qs[cur];
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r_lo = 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
-        const int r_hi = r_lo + 8;                // slots 8hh + 4..7
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const int col = 32 * b + tr_col;
-          const bf16x8 bb = cat8(ld_lds_tr(&b_tile[tile_off<D>(r_lo, col)]),
-                                 ld_lds_tr(&b_tile[tile_off<D>(r_hi, col)]));
-          acc_kd[b] = mfma32(as_bf16x8(opnd[t]), bb, acc_kd[b]);
+        for (int t = 0; t < 2; ++t) {
+          const int r_lo = 32 * qb + 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
+          const int r_hi = r_lo + 8;                          // slots 8hh + 4..7
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b) {
+            const int col = 32 * b + tr_col;
+            const bf16x8 bb = cat8(ld_lds_tr(&b_tile[tile_off<D>(r_lo, col)]),
+                                   ld_lds_tr(&b_tile[tile_off<D>(r_hi, col)]));
+            acc_kd[b] = mfma32(as_bf16x8(opnd[qb][t]), bb, acc_kd[b]);
+          }
         }
-      }
       __builtin_amdgcn_s_setprio(0);
     }
     if (it + 1 < nsteps) store_q(i + 1, cur ^ 1);
