@@ -142,17 +142,30 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     if (wave_active && j <= jw_last) {
       // S^T = K_j Q^T : two 32-key blocks, interleaved accumulation chains
+      // K fragments stream through a register ring PF k-steps deep, so each
+      // product's LDS read was issued several products earlier.
+      constexpr int PF = D / 16 < 4 ? D / 16 : 4;
       __builtin_amdgcn_s_setprio(1);
       f32x16 s[BC / 32];
+      bf16x8 kr[PF][BC / 32];
+#pragma unroll
+      for (int st = 0; st < PF; ++st)
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+          kr[st][kb] = ld_lds16(&ks[buf][tile_off<D>(32 * kb + l32, 16 * st + 8 * hh)]);
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads ahead of their use
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
+      for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb) {
-          const bf16x8 a = ld_lds16(&ks[buf][tile_off<D>(32 * kb + l32, 16 * st + 8 * hh)]);
-          s[kb] = mfma32(a, qf[st], s[kb]);
+          s[kb] = mfma32(kr[st % PF][kb], qf[st], s[kb]);
+          if (st + PF < D / 16)
+            kr[st % PF][kb] = ld_lds16(&ks[buf][tile_off<D>(32 * kb + l32, 16 * (st + PF) + 8 * hh)]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_s_setprio(0);
       // masks: causal (key > row) and sequence end (key >= N), only where needed
       const int kv0 = j * BC;
