@@ -10,17 +10,24 @@ causal, and 2.5 times that for the backward. The printed JSON line carries:
   value      whole-step (fwd + bwd) TFLOP/s
   fwd_*      the forward alone, the figure the 50%-of-peak target is set on
   roofline   the dominant launch (the one with the largest time share),
-             timed live with HIP events on the stream it runs on
+             timed live with HIP events on the stream it runs on; fa_bwd is
+             one launch sequence of three kernels and is timed as a unit
+  roofline_fwd  the same for fa_fwd
   cpu_baseline  the CPU fp64 oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "exact_tiled_attention_17_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_4x64x4096x128_causal.json")
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0
@@ -29,6 +36,29 @@ PEAK_HBM_GBS = 8000.0
 # Specifications) times for the same shapes on another GPU; context only.
 PAGE_TIMES_MS = {"2x8x512x64": 0.85, "4x32x1024x128": 2.1, "8x64x2048x128": 8.3,
                  "4x64x4096x128": 15.2}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(launch: str):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernels changed since the counters were taken (or none were taken)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch", {}).get(launch)
 
 
 def flops(w, causal):
@@ -74,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="c5", help="attn_inputs workload name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only fa_fwd (profiling aid)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before warmup, run one device-to-device copy of this many MiB "
+                         "(a known-size kernel to calibrate HBM byte counters against)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
@@ -99,6 +132,13 @@ def main():
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stream = torch.cuda.current_stream(dev)
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev is not None:
@@ -133,15 +173,17 @@ def main():
     step_flops = f_fwd + (0.0 if args.fwd_only else f_bwd)
     value = step_flops / (ms_step * 1e-3) / 1e12
 
-    if t_bwd >= t_fwd:
-        name, fl, tms = "fa_bwd (bwd_pre_kernel + bwd_kernel + bwd_dq_kernel)", f_bwd, t_bwd
-    else:
-        name, fl, tms = "fa_fwd (fwd_kernel)", f_fwd, t_fwd
-    achieved = fl / (tms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2),
+    def roof(launch, kernels, fl, tms):
+        achieved = fl / (tms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": f"{launch} ({kernels})", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(launch),
                 "avg_launch_ms": round(tms, 4)}
+
+    r_fwd = roof("fa_fwd", "fwd_kernel", f_fwd, t_fwd)
+    r_bwd = roof("fa_bwd", "bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel", f_bwd, t_bwd) \
+        if not args.fwd_only else None
+    roofline = r_bwd if (r_bwd is not None and t_bwd >= t_fwd) else r_fwd
 
     out = {
         "metric": "bf16 attention TFLOP/s fwd & fwd+bwd at 4x64x4096x128 causal, % MFMA peak",
@@ -168,6 +210,7 @@ def main():
         "fwd_bwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "page_context_ms": PAGE_TIMES_MS.get(w.label),
         "roofline": roofline,
+        "roofline_fwd": r_fwd,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
