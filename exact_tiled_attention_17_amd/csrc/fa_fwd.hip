@@ -35,36 +35,72 @@
 //  * The two waves sharing a SIMD raise their priority in their matrix-core
 //    phases, so one wave's softmax overlaps the other's products.
 
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 
-template <int D, int NW>
+template <int D>
 struct FwdCfg {
-  static constexpr int BR = 32 * NW;  // query rows per workgroup
-  static constexpr int BC = 64;       // keys per K/V tile
-  static constexpr int CH = D / 8;    // 16-byte chunks per row
+  static constexpr int NW = 8;         // two groups of 4 waves: one wave of each per SIMD
+  static constexpr int BR = 32 * NW;   // query rows per workgroup
+  static constexpr int BC = 64;        // keys per K/V tile
+  static constexpr int CH = D / 8;     // 16-byte chunks per row
   static constexpr int THREADS = 64 * NW;
-  static constexpr int LOADERS = THREADS / 2;  // half the threads load K, half V
-  static constexpr int TPT = BC * CH / LOADERS;  // 16-byte chunks per loader thread
-  static_assert(TPT >= 1 && BC * CH % LOADERS == 0, "loader split");
+  static constexpr int KST = D + 8;           // K tile row stride (elements): 16 bytes of padding
+  static constexpr int KCH = KST / 8;          // 16-byte chunk positions per K row
+  static constexpr int K_INSTR = BC * KCH / 64;  // direct-to-LDS instructions per K tile
+  static constexpr int V_INSTR = BC * CH / 64;   // ... per V tile
+  static_assert(BC * KCH % 64 == 0 && BC * CH % 64 == 0, "tile loads");
 };
 
-template <int D, int NW, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW)))
+// K tiles: row-major with rows padded by 16 bytes. The S^T products read
+// operand rows (16 consecutive keys at one chunk), which the padding spreads
+// over all banks; every read is one base address plus an immediate.
+// V tiles: row-major, 16-byte chunk c of row r at c ^ vswz(r). The transposing
+// reads of the V^T operand take 4 consecutive rows x 4 consecutive chunks; the
+// swizzle on the row's low bits puts those in distinct banks, and leaves the
+// address independent of the key step.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (D == 128) return (r & 3) << 2;
+  else return ((r >> 1) & 1) << 2;
+}
+template <int D>
+__device__ __forceinline__ int voff(int r, int col) {  // element offset of (r, col), col % 4 == 0
+  return r * D + (((col >> 3) ^ vswz<D>(r)) << 3) + (col & 4);
+}
+
+// Each wave alternates two phases per key tile t:
+//   M(t): S_{t+1} = K_{t+1} Q^T  and  O^T += V_t P_t^T      (matrix cores)
+//   V(t): online softmax of S_{t+1} -> P_{t+1}, rescale O    (vector ALUs)
+// (plus S_0 and softmax(S_0) up front). Group B (waves 4..7) runs one phase
+// behind group A (waves 0..3); each phase ends at a workgroup barrier, so on
+// every SIMD one wave's softmax runs while the other wave's products do.
+// Query rows are dealt in 32-row blocks alternating between the groups, so both
+// reach the causal diagonal on the same key tile.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O,
                 float* __restrict__ LSE, int N, int BH, float c_log2) {
-  using C = FwdCfg<D, NW>;
+  using C = FwdCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, CH = C::CH;
   // Lazy rescaling: the running max used for P only moves when the true row
   // max exceeds it by more than TAU (base-2 units), so P <= 2^TAU and the
   // O^T rescale is skipped on most tiles. The result is exact either way:
   // O = sum_j 2^(c s_j - m) v_j / sum_j 2^(c s_j - m) for any common m.
   constexpr float TAU = 8.f;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BC * D];  // K tiles, row-major
-  __shared__ __attribute__((aligned(16))) __bf16 vs[2][BC * D];  // V tiles, row-major
+  constexpr int KST = C::KST, KCH = C::KCH;
+  // Double-buffered tiles as four separate arrays: every access names its
+  // buffer statically, so the compiler can tell that the tile loads in flight
+  // do not write what the current products read (and waits for none of them).
+  __shared__ __attribute__((aligned(16))) __bf16 ks0[BC * KST];  // K tiles, padded rows
+  __shared__ __attribute__((aligned(16))) __bf16 ks1[BC * KST];
+  __shared__ __attribute__((aligned(16))) __bf16 vs0[BC * D];    // V tiles, swizzled
+  __shared__ __attribute__((aligned(16))) __bf16 vs1[BC * D];
 
   const int nq = (N + BR - 1) / BR;
   int bh, qt;
@@ -76,8 +112,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int tr_grp = lane >> 4, tr_i = lane & 15;         // transposing-read addressing
+  const int grp = wave >> 2;                        // 0: group A, 1: group B
+  const int rblk = 2 * (wave & 3) + grp;            // this wave's 32-row block
+  const int tr_grp = lane >> 4, tr_i = lane & 15;   // transposing-read addressing
   const int tr_e = tr_i >> 2;
+  const int wl = wave & 3;  // wave index within its group
   const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);
 
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -87,13 +126,14 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rV = make_rsrc(V + head, head_bytes);
 
   const int q0 = qt * BR;
-  const int wrow0 = q0 + 32 * wave;  // first query row of this wave
+  const int wrow0 = q0 + 32 * rblk;  // first query row of this wave
   const int row = wrow0 + l32;       // this lane's query row
   const int nkv_all = (N + BC - 1) / BC;
   const int last_row_wg = min(q0 + BR, N) - 1;
-  const int nkv = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;
+  const int T = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;  // key tiles
   const bool wave_active = wrow0 < N;
-  const int jw_last = CAUSAL ? min(wrow0 + 31, N - 1) / BC : nkv - 1;
+  // last key tile this wave needs (-1: none)
+  const int jw_last = !wave_active ? -1 : CAUSAL ? min(wrow0 + 31, N - 1) / BC : T - 1;
 
   // ---- Q^T operand: lane holds row `row`, d = 16 s + 8 hh .. +7 (0 past N) --
   bf16x8 qf[D / 16];
@@ -101,137 +141,223 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int s = 0; s < D / 16; ++s)
     qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
 
-  // ---- K/V tile staging: waves 0..NW/2-1 load K, the rest V (wave-uniform);
-  // both tiles row-major with the chunk swizzle of tile_off ---------------------
-  const bool k_loader = wave < NW / 2;
-  const int lt = tid % C::LOADERS;
-  const auto rT = k_loader ? rK : rV;
-  u32x4 stg[C::TPT];
-  auto load_tile = [&](int j) {
+  // ---- K/V tiles, straight from HBM into LDS: one instruction fills 64
+  // consecutive 16-byte chunk positions of a tile, each lane fetching the global
+  // chunk that the tile layout puts at its position. The instructions of a tile
+  // are dealt round-robin over NL loader waves (w = index among them).
+  // The per-lane source offsets are recomputed at each use (a few integer ops)
+  // rather than kept live across the loop, where they would cost registers.
+  auto opaque_lane = [&]() {
+    int x = lane;
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  // (K: padding positions fetch chunk 0 again)
+  auto load_k = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
+    constexpr int nl = decltype(NL)::value;
+    const int ln = opaque_lane();
 #pragma unroll
-    for (int r = 0; r < C::TPT; ++r) {
-      const int i = lt + r * C::LOADERS;
-      stg[r] = buf_load16(rT, (uint32_t)(j * BC + i / CH) * (D * 2) + (i % CH) * 16);
+    for (int n0 = 0; n0 < C::K_INSTR; n0 += nl) {
+      const int n = n0 + w;
+      if (n < C::K_INSTR) {
+        const int i = 64 * n + ln;
+        const int kr = i / KCH, pos = i % KCH;
+        buf_load16_lds(rK, (uint32_t)(j * BC + kr) * (D * 2) + (pos < CH ? pos * 16 : 0),
+                       t + 64 * n * 8);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-    __bf16* t = k_loader ? ks[buf] : vs[buf];
+  auto load_v = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
+    constexpr int nl = decltype(NL)::value;
+    const int ln = opaque_lane();
 #pragma unroll
-    for (int r = 0; r < C::TPT; ++r) {
-      const int i = lt + r * C::LOADERS;
-      st_lds16(&t[tile_off<D>(i / CH, 8 * (i % CH))], stg[r]);
+    for (int n0 = 0; n0 < C::V_INSTR; n0 += nl) {
+      const int n = n0 + w;
+      if (n < C::V_INSTR) {
+        const int i = 64 * n + ln;
+        const int vr = i / CH, pos = i % CH;
+        buf_load16_lds(rV, (uint32_t)(j * BC + vr) * (D * 2) + ((pos ^ vswz<D>(vr)) * 16),
+                       t + 64 * n * 8);
+      }
     }
   };
+  using four = std::integral_constant<int, 4>;
+  using eight = std::integral_constant<int, 8>;
 
   // ---- running state ----------------------------------------------------------
   f32x16 o[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
+  f32x16 sacc[BC / 32];     // S^T of the tile being processed
+  u32x4 pf[BC / 16];        // P^T of the previous tile, bf16, as B operands
   float m_run = -INFINITY;  // reference max of c * s for this row (base-2 units)
   float l_run = 0.f;        // this lane's share of the running sum
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_tile(0);
-  store_tile(0);
+  // online softmax of sacc (key tile u) -> pf; rescales o, l
+  auto softmax = [&](int u) __attribute__((always_inline)) {
+    const int kv0 = u * BC;
+    const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= N || (CAUSAL && key > row)) sacc[kb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = pair_max(mx) * c_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+    }
+    const float neg_m = -m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][8 * t + 2 * e], c_log2, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][8 * t + 2 * e + 1], c_log2, neg_m));
+          const uint32_t pk = pack_bf16(p0, p1);
+          pf[2 * kb + t][e] = pk;
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
+        }
+    l_run += lsum;
+  };
+
+  // M phase: S_u = K_u Q^T into sacc (if DO_S) and O^T += V_t P_t^T (if DO_PV),
+  // the two product streams interleaved. Operands stream through register rings
+  // two products deep (fenced so the scheduler keeps that depth instead of
+  // hoisting every read, which would not fit the register budget).
+  auto mphase = [&](auto DO_S, auto DO_PV, const __bf16* kt, const __bf16* vt) __attribute__((always_inline)) {
+    constexpr bool do_s = decltype(DO_S)::value, do_pv = decltype(DO_PV)::value;
+    constexpr int NM = (D / 16) * (BC / 32);  // = (BC / 16) * (D / 32): products per stream
+    auto kread = [&](int i) {  // K fragment of S product i (k-step i / 2, key block i % 2)
+      const int st = i / (BC / 32), kb = i % (BC / 32);
+      return ld_lds16(&kt[(32 * kb + l32) * KST + 16 * st + 8 * hh]);
+    };
+    auto vread = [&](int i) {  // V^T fragment of PV product i (key step i / 4, d block i % 4)
+      const int tk = i / (D / 32), b = i % (D / 32);
+      const int r_lo = 16 * tk + 4 * hh + tr_e;  // slots 8hh + 0..3
+      const int col = 32 * b + tr_col;
+      return cat8(ld_lds_tr(&vt[voff<D>(r_lo, col)]),
+                  ld_lds_tr(&vt[voff<D>(r_lo + 8, col)]));  // slots 8hh + 4..7
+    };
+    bf16x8 kr[2], vr[2];
+    if constexpr (do_s) {
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) sacc[kb] = f32x16{};
+      kr[0] = kread(0);
+      kr[1] = kread(1);
+    }
+    if constexpr (do_pv) {
+      vr[0] = vread(0);
+      vr[1] = vread(1);
+    }
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if constexpr (do_s) {
+        const int st = i / (BC / 32), kb = i % (BC / 32);
+        sacc[kb] = mfma32(kr[i & 1], qf[st], sacc[kb]);
+        if (i + 2 < NM) kr[i & 1] = kread(i + 2);
+      }
+      if constexpr (do_pv) {
+        const int tk = i / (D / 32), b = i % (D / 32);
+        o[b] = mfma32(vr[i & 1], as_bf16x8(pf[tk]), o[b]);
+        if (i + 2 < NM) vr[i & 1] = vread(i + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+
+  // Workgroup barrier without a memory fence: the LDS reads of a phase are all
+  // consumed by its own products before it ends, and tile loads are waited for
+  // explicitly (a fenced barrier would also wait for the loads still meant to
+  // be in flight). The asm keeps the compiler from moving memory accesses
+  // across it.
+  auto slot_barrier = [] { asm volatile("s_barrier" ::: "memory"); };
+
+  // ---- schedule ----------------------------------------------------------------
+  // Barrier-delimited slots. Group A runs S_0 in slot 0, then softmax(t) in
+  // slot 2t+1 and M(t) in slot 2t+2; group B runs the same sequence one slot
+  // later (it waits out slot 0, group A waits out the last slot), so in every
+  // slot from 1 on one group's products overlap the other's softmax. Both
+  // groups run straight-line code: no phase is conditional, which keeps the
+  // accumulators in place across the loop.
+  // Tiles: K_0, K_1 and V_0 are loaded up front. Group B issues K_{t+2} (into
+  // the buffer of K_t) and V_{t+1} (into that of V_{t-1}) at the start of its
+  // softmax(t), slot 2t+2, after the last reads of those buffers (slot 2t+1),
+  // and waits for them at the end of its M(t), slot 2t+3; their first reader is
+  // group A's M(t+1) in slot 2t+4.
+  load_k(eight{}, wave, 0, ks0);
+  if (T > 1) load_k(eight{}, wave, 1, ks1);
+  load_v(eight{}, wave, 0, vs0);
   wait_vmem_all();
   __syncthreads();
-
-  for (int j = 0; j < nkv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkv) load_tile(j + 1);
-
-    if (wave_active && j <= jw_last) {
-      // S^T = K_j Q^T : two 32-key blocks, interleaved accumulation chains
-      // K fragments stream through a register ring PF k-steps deep, so each
-      // product's LDS read was issued several products earlier.
-      constexpr int PF = D / 16 < 4 ? D / 16 : 4;
-      __builtin_amdgcn_s_setprio(1);
-      f32x16 s[BC / 32];
-      bf16x8 kr[PF][BC / 32];
-#pragma unroll
-      for (int st = 0; st < PF; ++st)
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-          kr[st][kb] = ld_lds16(&ks[buf][tile_off<D>(32 * kb + l32, 16 * st + 8 * hh)]);
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads ahead of their use
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
-          s[kb] = mfma32(kr[st % PF][kb], qf[st], s[kb]);
-          if (st + PF < D / 16)
-            kr[st % PF][kb] = ld_lds16(&ks[buf][tile_off<D>(32 * kb + l32, 16 * (st + PF) + 8 * hh)]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // masks: causal (key > row) and sequence end (key >= N), only where needed
-      const int kv0 = j * BC;
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= N || (CAUSAL && key > row)) s[kb][r] = -INFINITY;
-          }
-      }
-      // online softmax (base 2) with lazy rescaling
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = pair_max(mx) * c_log2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
-      }
-      const float neg_m = -m_run;
-
-      u32x4 pf[BC / 16];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e], c_log2, neg_m));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * t + 2 * e + 1], c_log2, neg_m));
-            const uint32_t pk = pack_bf16(p0, p1);
-            pf[2 * kb + t][e] = pk;
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
-          }
-      l_run += lsum;
-
-      // O^T += V^T P^T; V^T by transposing reads, keys in the P^T slot order
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int t = 0; t < BC / 16; ++t) {
-        const int r_lo = 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
-        const int r_hi = r_lo + 8;                // slots 8hh + 4..7
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const int col = 32 * b + tr_col;
-          const bf16x8 a = cat8(ld_lds_tr(&vs[buf][tile_off<D>(r_lo, col)]),
-                                ld_lds_tr(&vs[buf][tile_off<D>(r_hi, col)]));
-          o[b] = mfma32(a, as_bf16x8(pf[t]), o[b]);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
+  if (grp == 1) __syncthreads();
+  mphase(yes{}, no{}, ks0, vs0);  // S_0
+  slot_barrier();
+  // one tile, t: buffers of parity P = t & 1 (static in each copy)
+  auto tile = [&](auto P, int t) __attribute__((always_inline)) {
+    constexpr bool odd = decltype(P)::value;
+    __bf16* k_this = odd ? ks1 : ks0;  // K_t, refilled with K_{t+2}
+    __bf16* k_next = odd ? ks0 : ks1;  // K_{t+1}
+    __bf16* v_this = odd ? vs1 : vs0;  // V_t
+    __bf16* v_next = odd ? vs0 : vs1;  // V_{t+1}, loaded now
+    if (grp == 1) {
+      if (t + 2 < T) load_k(four{}, wl, t + 2, k_this);
+      if (t + 1 < T) load_v(four{}, wl, t + 1, v_next);
     }
-
-    if (j + 1 < nkv) store_tile(buf ^ 1);
-    __syncthreads();
+    softmax(t);
+    slot_barrier();
+    mphase(yes{}, yes{}, k_next, v_this);
+    wait_vmem_all();  // (group A has none in flight; waiting on every wave keeps the
+    slot_barrier();   //  compiler's view of pending loads exact)
+  };
+  using even_t = std::false_type;
+  using odd_t = std::true_type;
+  int t = 0;
+  // tiles with unmasked keys for this wave's rows (M(t) of the last one also
+  // computes an unused S_{t+1}, from whatever its buffer holds)
+  for (; t + 1 <= jw_last; t += 2) {
+    tile(even_t{}, t);
+    tile(odd_t{}, t + 1);
   }
+  if (t <= jw_last) tile(even_t{}, t++);
+  // tiles whose keys are all masked for this wave's rows: keep to the schedule
+  for (; t < T; ++t) {
+    if (grp == 1) {
+      if (t & 1) {
+        if (t + 2 < T) load_k(four{}, wl, t + 2, ks1);
+        if (t + 1 < T) load_v(four{}, wl, t + 1, vs0);
+      } else {
+        if (t + 2 < T) load_k(four{}, wl, t + 2, ks0);
+        if (t + 1 < T) load_v(four{}, wl, t + 1, vs1);
+      }
+    }
+    slot_barrier();
+    wait_vmem_all();
+    slot_barrier();
+  }
+  if (grp == 0) slot_barrier();
 
   // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l) ------------------------
   if (!wave_active) return;
@@ -252,19 +378,19 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     LSE[(size_t)bh * N + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  using C = FwdCfg<D, NW>;
+  using C = FwdCfg<D>;
   const int nq = (a.N + C::BR - 1) / C::BR;
   const long long total = (long long)nq * a.B * a.H;
-  return launch_kernel(fwd_kernel<D, NW, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+  return launch_kernel(fwd_kernel<D, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
                        a.LSE, a.N, a.B * a.H, a.softmax_scale * kLog2e);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_fwd_t<128, 8, true>(a) : launch_fwd_t<128, 8, false>(a);
-  return a.causal ? launch_fwd_t<64, 4, true>(a) : launch_fwd_t<64, 4, false>(a);
+  if (a.d == 128) return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
+  return a.causal ? launch_fwd_t<64, true>(a) : launch_fwd_t<64, false>(a);
 }
 
 }  // namespace fa
