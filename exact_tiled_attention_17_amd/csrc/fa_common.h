@@ -69,12 +69,13 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
-// lds_base + 16 l (lds_base is wave-uniform), the global source is per lane.
-// Completion is tracked by vmcnt, like any vector-memory load.
-__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+// lds_base + 16 l (lds_base is wave-uniform); the source is byte voff (per
+// lane) + soff (wave-uniform) of the buffer. Completion is tracked by vmcnt,
+// like any vector-memory load.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                                __bf16* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           byte_off, 0, 0, 0);
+                                           voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {

@@ -94,6 +94,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // O = sum_j 2^(c s_j - m) v_j / sum_j 2^(c s_j - m) for any common m.
   constexpr float TAU = 8.f;
   constexpr int KST = C::KST, KCH = C::KCH;
+  constexpr int RING = 2;  // operand reads in flight ahead of their products, per stream
   // Double-buffered tiles as four separate arrays: every access names its
   // buffer statically, so the compiler can tell that the tile loads in flight
   // do not write what the current products read (and waits for none of them).
@@ -141,44 +142,44 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int s = 0; s < D / 16; ++s)
     qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
 
-  // ---- K/V tiles, straight from HBM into LDS: one instruction fills 64
-  // consecutive 16-byte chunk positions of a tile, each lane fetching the global
-  // chunk that the tile layout puts at its position. The instructions of a tile
-  // are dealt round-robin over NL loader waves (w = index among them).
-  // The per-lane source offsets are recomputed at each use (a few integer ops)
-  // rather than kept live across the loop, where they would cost registers.
-  auto opaque_lane = [&]() {
-    int x = lane;
-    asm volatile("" : "+v"(x));
-    return x;
+  // ---- K/V tiles, straight from HBM into LDS: instruction n of a tile fills
+  // the 64 consecutive 16-byte chunk positions [64 n, 64 n + 64) of the tile's
+  // LDS image, each lane fetching the global chunk that the layout puts at its
+  // position. The instructions of a tile are dealt round-robin over NL loader
+  // waves (w = index among them). Source offsets are split into a per-lane part
+  // (below, relative to the tile's first row) and the tile's row offset, which
+  // goes in the scalar offset.
+  auto k_src = [&](int n) -> uint32_t {  // padding positions fetch chunk 0 again
+    const int i = 64 * n + lane;
+    const int kr = i / KCH, pos = i % KCH;
+    return (uint32_t)(kr * (D * 2) + (pos < CH ? pos * 16 : 0));
   };
-  // (K: padding positions fetch chunk 0 again)
+  // V: 64 positions are whole rows (64 / CH of them, a multiple of the swizzle
+  // period), so instruction n's offsets are instruction 0's plus 1024 n bytes.
+  const uint32_t v_src0 = (uint32_t)((lane / CH) * (D * 2) + (((lane % CH) ^ vswz<D>(lane / CH)) * 16));
+  // this wave's K offsets as one of the four in-loop loaders (n = wl + 4 m)
+  constexpr int KM = (C::K_INSTR + 3) / 4;
+  uint32_t k_src_b[KM];
+#pragma unroll
+  for (int m = 0; m < KM; ++m) k_src_b[m] = k_src(wl + 4 * m);
+
   auto load_k = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
     constexpr int nl = decltype(NL)::value;
-    const int ln = opaque_lane();
+    const uint32_t row0 = (uint32_t)j * (BC * D * 2);
 #pragma unroll
-    for (int n0 = 0; n0 < C::K_INSTR; n0 += nl) {
-      const int n = n0 + w;
-      if (n < C::K_INSTR) {
-        const int i = 64 * n + ln;
-        const int kr = i / KCH, pos = i % KCH;
-        buf_load16_lds(rK, (uint32_t)(j * BC + kr) * (D * 2) + (pos < CH ? pos * 16 : 0),
-                       t + 64 * n * 8);
-      }
+    for (int m = 0; m * nl < C::K_INSTR; ++m) {
+      const int n = m * nl + w;
+      if (n < C::K_INSTR)
+        buf_load16_lds(rK, nl == 4 ? k_src_b[m] : k_src(n), row0, t + 64 * n * 8);
     }
   };
   auto load_v = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
     constexpr int nl = decltype(NL)::value;
-    const int ln = opaque_lane();
+    const uint32_t row0 = (uint32_t)j * (BC * D * 2);
 #pragma unroll
-    for (int n0 = 0; n0 < C::V_INSTR; n0 += nl) {
-      const int n = n0 + w;
-      if (n < C::V_INSTR) {
-        const int i = 64 * n + ln;
-        const int vr = i / CH, pos = i % CH;
-        buf_load16_lds(rV, (uint32_t)(j * BC + vr) * (D * 2) + ((pos ^ vswz<D>(vr)) * 16),
-                       t + 64 * n * 8);
-      }
+    for (int m = 0; m * nl < C::V_INSTR; ++m) {
+      const int n = m * nl + w;
+      if (n < C::V_INSTR) buf_load16_lds(rV, v_src0, row0 + 1024u * n, t + 64 * n * 8);
     }
   };
   using four = std::integral_constant<int, 4>;
@@ -256,16 +257,17 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       return cat8(ld_lds_tr(&vt[voff<D>(r_lo, col)]),
                   ld_lds_tr(&vt[voff<D>(r_lo + 8, col)]));  // slots 8hh + 4..7
     };
-    bf16x8 kr[2], vr[2];
+    constexpr int R = RING;
+    bf16x8 kr[R], vr[R];
     if constexpr (do_s) {
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) sacc[kb] = f32x16{};
-      kr[0] = kread(0);
-      kr[1] = kread(1);
+#pragma unroll
+      for (int j = 0; j < R; ++j) kr[j] = kread(j);
     }
     if constexpr (do_pv) {
-      vr[0] = vread(0);
-      vr[1] = vread(1);
+#pragma unroll
+      for (int j = 0; j < R; ++j) vr[j] = vread(j);
     }
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -273,13 +275,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int i = 0; i < NM; ++i) {
       if constexpr (do_s) {
         const int st = i / (BC / 32), kb = i % (BC / 32);
-        sacc[kb] = mfma32(kr[i & 1], qf[st], sacc[kb]);
-        if (i + 2 < NM) kr[i & 1] = kread(i + 2);
+        sacc[kb] = mfma32(kr[i % R], qf[st], sacc[kb]);
+        if (i + R < NM) kr[i % R] = kread(i + R);
       }
       if constexpr (do_pv) {
         const int tk = i / (D / 32), b = i % (D / 32);
-        o[b] = mfma32(vr[i & 1], as_bf16x8(pf[tk]), o[b]);
-        if (i + 2 < NM) vr[i & 1] = vread(i + 2);
+        o[b] = mfma32(vr[i % R], as_bf16x8(pf[tk]), o[b]);
+        if (i + R < NM) vr[i % R] = vread(i + R);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
