@@ -17,23 +17,24 @@
 //    the second product (no LDS round trip); the V^T operand comes from the
 //    row-major V tile through gfx950's transposing LDS read, rows taken in the
 //    key order of the P^T operand.
-//  * K/V tiles of BC = 64 keys are staged in LDS, double buffered: the global
-//    loads of tile j+1 are issued before tile j is computed and written to LDS
-//    after it, one barrier per tile. Both tiles are row-major with an XOR
-//    swizzle on 16-byte chunks that keeps operand-row reads and transposing
-//    reads free of bank conflicts.
+//  * K/V tiles of BC = 64 keys are staged in LDS, double buffered, and loaded
+//    straight from HBM into LDS (buffer loads with the LDS destination), so no
+//    registers carry tile data. K rows are padded by 16 bytes; V rows carry an
+//    XOR swizzle on 16-byte chunks; both keep the operand reads free of bank
+//    conflicts.
+//  * The eight waves form two groups that run the same phase sequence one
+//    phase apart (a ping-pong): while one wave of a SIMD runs its products,
+//    the other runs its softmax. Each phase ends at a workgroup barrier.
 //  * Causal: tiles entirely above the diagonal are never loaded; a wave skips
-//    tiles fully masked for its own rows; masks are applied only to tiles that
-//    cross the diagonal or the end of the sequence.
+//    the work of tiles fully masked for its own rows; masks are applied only to
+//    tiles that cross the diagonal or the end of the sequence.
 //  * The softmax runs in base 2 in float32: c = scale * log2(e) is folded into
-//    one FMA per score; P is rounded to bf16 for the matrix core and the row
-//    sum l is accumulated from those same rounded values (dot2 with 1s). The
-//    reference max only moves when the row max outgrows it by 2^8, so the
-//    O^T rescale runs on few tiles.
+//    one FMA per score; P is rounded to bf16 for the matrix core, the row sum l
+//    is accumulated in float32 from the unrounded values. The reference max
+//    only moves when the row max outgrows it by 2^8, so the O^T rescale runs on
+//    few tiles.
 //  * Global reads go through buffer resources: rows past the end of the
 //    sequence read as zeros, with no branches around the loads.
-//  * The two waves sharing a SIMD raise their priority in their matrix-core
-//    phases, so one wave's softmax overlaps the other's products.
 
 #include <type_traits>
 
@@ -193,7 +194,6 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   u32x4 pf[BC / 16];        // P^T of the previous tile, bf16, as B operands
   float m_run = -INFINITY;  // reference max of c * s for this row (base-2 units)
   float l_run = 0.f;        // this lane's share of the running sum
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // online softmax of sacc (key tile u) -> pf; rescales o, l
   auto softmax = [&](int u) __attribute__((always_inline)) {
@@ -234,10 +234,21 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][8 * t + 2 * e + 1], c_log2, neg_m));
           const uint32_t pk = pack_bf16(p0, p1);
           pf[2 * kb + t][e] = pk;
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
+          lsum += p0 + p1;
         }
     l_run += lsum;
   };
+
+  // Per-lane element offsets of the transposing V^T reads, one per d block:
+  // the swizzle of row 16 tk + 4 hh + tr_e (and of that row + 8) depends only on
+  // tr_e, so the key step tk adds a constant. Kept live across the loop (the
+  // asm stops the compiler from recomputing them in every product phase).
+  int vrow[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) {
+    vrow[b] = voff<D>(4 * hh + tr_e, 32 * b + tr_col);
+    asm volatile("" : "+v"(vrow[b]));
+  }
 
   // M phase: S_u = K_u Q^T into sacc (if DO_S) and O^T += V_t P_t^T (if DO_PV),
   // the two product streams interleaved. Operands stream through register rings
@@ -252,10 +263,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     };
     auto vread = [&](int i) {  // V^T fragment of PV product i (key step i / 4, d block i % 4)
       const int tk = i / (D / 32), b = i % (D / 32);
-      const int r_lo = 16 * tk + 4 * hh + tr_e;  // slots 8hh + 0..3
-      const int col = 32 * b + tr_col;
-      return cat8(ld_lds_tr(&vt[voff<D>(r_lo, col)]),
-                  ld_lds_tr(&vt[voff<D>(r_lo + 8, col)]));  // slots 8hh + 4..7
+      const __bf16* p = vt + vrow[b] + 16 * tk * D;  // rows 16 tk + 4 hh + tr_e: slots 8hh + 0..3
+      return cat8(ld_lds_tr(p), ld_lds_tr(p + 8 * D));  // rows + 8: slots 8hh + 4..7
     };
     constexpr int R = RING;
     bf16x8 kr[R], vr[R];
@@ -294,8 +303,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // consumed by its own products before it ends, and tile loads are waited for
   // explicitly (a fenced barrier would also wait for the loads still meant to
   // be in flight). The asm keeps the compiler from moving memory accesses
-  // across it.
-  auto slot_barrier = [] { asm volatile("s_barrier" ::: "memory"); };
+  // across it, the scheduling fences keep all other instructions on their side
+  // (leftover softmax work moved into a product phase would delay its products).
+  auto slot_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // ---- schedule ----------------------------------------------------------------
   // Barrier-delimited slots. Group A runs S_0 in slot 0, then softmax(t) in
