@@ -28,6 +28,8 @@
 // Global reads go through buffer resources, so rows past the end of the
 // sequence read as zeros without branches.
 
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -289,36 +291,50 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // ---------------------------------------------------------------------------
 // 3. dQ kernel
 // ---------------------------------------------------------------------------
-// One workgroup per (batch, head, tile of 32*NW queries); each wave owns 32
-// query rows and sweeps the key tiles like the forward kernel does, with the
-// products transposed so that a lane owns one query:
+// One workgroup per (batch, head, tile of 256 queries); each of its 8 waves
+// owns 32 query rows and sweeps the key tiles like the forward kernel, with
+// the products transposed so that a lane owns one query:
 //   S^T = K_j Q^T, dP^T = V_j dO^T     (lane = one query, 16 keys per block)
 //   P^T = exp2(c S^T - LSE2), dS^T = P^T (dP^T - D)   (LSE2, D: the lane's own)
 //   dQ^T += K_j^T dS^T                 (dS^T straight from registers; K_j^T
 //                                       by transposing reads of the K tile)
 // and writes dQ = scale * dQ^T as bf16. No atomics: each dQ row is summed
 // over all keys inside one wave.
-template <int D, int NW>
+// The schedule is the forward's two-group ping-pong: a wave alternates
+//   M(t): dQ^T += K_t^T dS^T_t, then S^T_{t+1}, dP^T_{t+1}   (matrix cores)
+//   V(t): dS^T_t from S^T_t, dP^T_t                          (vector ALUs)
+// with the second group one phase behind, so on every SIMD one wave's dS
+// overlaps the other's products. K_t is read in M(t) as well as (for S_t) in
+// M(t-1), so K tiles are kept in four buffers, V tiles in two; all are loaded
+// straight from HBM into LDS.
+template <int D>
 struct DqCfg {
-  static constexpr int BR = 32 * NW;  // query rows per workgroup
-  static constexpr int BC = 64;       // keys per K/V tile
-  static constexpr int CH = D / 8;
+  static constexpr int NW = 8;          // two groups of 4 waves
+  static constexpr int BR = 32 * NW;    // query rows per workgroup
+  static constexpr int BC = 64;         // keys per K/V tile
+  static constexpr int CH = D / 8;      // 16-byte chunks per row
   static constexpr int THREADS = 64 * NW;
-  static constexpr int LOADERS = THREADS / 2;  // half load K, half V
-  static constexpr int TPT = BC * CH / LOADERS;
-  static_assert(TPT >= 1 && BC * CH % LOADERS == 0, "loaders");
+  static constexpr int TI = BC * CH / 64;  // direct-to-LDS instructions per tile
+  static_assert(BC * CH % 64 == 0, "tile loads");
 };
 
-template <int D, int NW, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW)))
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const f32x2* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
                    float c_log2, float scale) {
-  using C = DqCfg<D, NW>;
-  constexpr int BR = C::BR, BC = C::BC, CH = C::CH;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BC * D];  // K tiles, row-major
-  __shared__ __attribute__((aligned(16))) __bf16 vs[2][BC * D];  // V tiles, row-major
+  using C = DqCfg<D>;
+  constexpr int BR = C::BR, BC = C::BC, CH = C::CH, TI = C::TI;
+  // K tiles in four buffers, V tiles in two; separate arrays so that every
+  // access names its buffer statically. Row-major, 16-byte chunk c of row r at
+  // c ^ swz(r): conflict-free for operand-row reads and transposing reads.
+  __shared__ __attribute__((aligned(16))) __bf16 ks0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 ks1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 ks2[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 ks3[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs1[BC * D];
 
   const int nq = (N + BR - 1) / BR;
   int bh, qt;
@@ -330,9 +346,12 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int tr_grp = lane >> 4, tr_i = lane & 15;
+  const int grp = wave >> 2;              // 0: group A, 1: group B
+  const int wl = wave & 3;                // wave index within its group
+  const int rblk = 2 * wl + grp;          // this wave's 32-row block
+  const int tr_i = lane & 15;
   const int tr_e = tr_i >> 2;
-  const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -343,13 +362,14 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rRS = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 8u);
 
   const int q0 = qt * BR;
-  const int wrow0 = q0 + 32 * wave;
+  const int wrow0 = q0 + 32 * rblk;
   const int row = wrow0 + l32;
   const int nkv_all = (N + BC - 1) / BC;
   const int last_row_wg = min(q0 + BR, N) - 1;
-  const int nkv = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;
+  const int T = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;  // key tiles
   const bool wave_active = wrow0 < N;
-  const int jw_last = CAUSAL ? min(wrow0 + 31, N - 1) / BC : nkv - 1;
+  // last key tile this wave needs (-1: none)
+  const int jw_last = !wave_active ? -1 : CAUSAL ? min(wrow0 + 31, N - 1) / BC : T - 1;
 
   // Q^T and dO^T operands (rows past N read as zeros) and the row statistics
   bf16x8 qf[D / 16], of[D / 16];
@@ -363,99 +383,204 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       f32x2, __builtin_amdgcn_raw_buffer_load_b64(rRS, (uint32_t)row * 8u, 0, 0));
   const float neg_l2 = -rst[0], dval = rst[1];
 
-  // K / V tile loaders (wave-uniform roles), row-major swizzled tiles
-  const bool k_loader = wave < NW / 2;
-  const int lt = tid % C::LOADERS;
-  const auto rT = k_loader ? rK : rV;
-  u32x4 stg[C::TPT];
-  auto load_tile = [&](int j) {
+  // ---- tile loads, straight from HBM into LDS: instruction n of a tile fills
+  // chunk positions [64 n, 64 n + 64); each lane fetches the chunk the layout
+  // puts at its position. K and V tiles share the layout, hence the offsets.
+  auto src = [&](int n) -> uint32_t {
+    const int p = 64 * n + lane;
+    const int r = p / CH, pc = p % CH;
+    return (uint32_t)(r * (D * 2) + ((pc ^ swz<D>(r)) * 16));
+  };
+  constexpr int LM = (TI + 3) / 4;
+  uint32_t src_b[LM];  // this wave's offsets as one of the four in-loop loaders
 #pragma unroll
-    for (int r = 0; r < C::TPT; ++r) {
-      const int i = lt + r * C::LOADERS;
-      stg[r] = buf_load16(rT, (uint32_t)(j * BC + i / CH) * (D * 2) + (i % CH) * 16);
+  for (int m = 0; m < LM; ++m) src_b[m] = src(wl + 4 * m);
+  auto load_tile = [&](auto NL, __amdgpu_buffer_rsrc_t rsrc, int w, int j, __bf16* t)
+      __attribute__((always_inline)) {
+    constexpr int nl = decltype(NL)::value;
+    const uint32_t row0 = (uint32_t)j * (BC * D * 2);
+#pragma unroll
+    for (int m = 0; m * nl < TI; ++m) {
+      const int n = m * nl + w;
+      if (n < TI) buf_load16_lds(rsrc, nl == 4 ? src_b[m] : src(n), row0, t + 64 * n * 8);
     }
   };
-  auto store_tile = [&](int buf) {
-    __bf16* t = k_loader ? ks[buf] : vs[buf];
-#pragma unroll
-    for (int r = 0; r < C::TPT; ++r) {
-      const int i = lt + r * C::LOADERS;
-      st_lds16(&t[tile_off<D>(i / CH, 8 * (i % CH))], stg[r]);
-    }
-  };
+  using four = std::integral_constant<int, 4>;
+  using eight = std::integral_constant<int, 8>;
 
-  f32x16 acc[D / 32];
+  // ---- LDS read offsets (elements) -----------------------------------------------
+  // With the swizzle, the operand-row read of k-step st (row 32 kb + l32, chunk
+  // 2 st + hh) sits at rw ^ 16 st (+ 32 kb D), and the transposing read of d
+  // block b (rows 16 t + 4 hh + tr_e, and + 8; column 32 b + tr_col) at
+  // tw ^ 32 b (+ 16 t D): one register each, one XOR per read.
+  int rw = tile_off<D>(l32, 8 * hh);
+  int tw0 = tile_off<D>(4 * hh + tr_e, tr_col);
+  int tw1 = tile_off<D>(4 * hh + tr_e + 8, tr_col);
+  asm volatile("" : "+v"(rw), "+v"(tw0), "+v"(tw1));
+
+  // ---- running state -----------------------------------------------------------
+  f32x16 acc[D / 32];  // dQ^T: M = d, N = this wave's 32 queries
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
+  f32x16 s[BC / 32], dp[BC / 32];  // S^T, dP^T of the tile in flight
+  u32x4 dsf[BC / 16];              // dS^T as B operands, 4 k-steps of 16 keys
 
-  load_tile(0);
-  store_tile(0);
-  wait_vmem_all();
-  __syncthreads();
+  // V(u): dS^T of key tile u from s, dp
+  auto vphase = [&](int u) __attribute__((always_inline)) {
+    const int kv0 = u * BC;
+    const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
+    // key kv0 + 32 kb + 8 (r / 4) + 4 hh + r % 4 is masked iff its offset
+    // 32 kb + 8 (r / 4) + r % 4 exceeds lim (one compare with a constant)
+    const int lim = (CAUSAL ? min(row, N - 1) : N - 1) - kv0 - 4 * hh;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float d2[2];
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][r + u2], c_log2, neg_l2));
+          d2[u2] = p * (dp[kb][r + u2] - dval);
+          // dS itself is zeroed: a masked tile may hold stale data
+          if (need_mask && 32 * kb + 8 * ((r + u2) >> 2) + ((r + u2) & 3) > lim) d2[u2] = 0.f;
+        }
+        dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16(d2[0], d2[1]);
+      }
+  };
 
-  for (int j = 0; j < nkv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkv) load_tile(j + 1);
-
-    if (wave_active && j <= jw_last) {
-      // S^T = K_j Q^T and dP^T = V_j dO^T: two 32-key blocks each
-      f32x16 s[BC / 32], dp[BC / 32];
+  // M phase: dQ^T += K_t^T dS^T_t (if DO_DQ), then S^T, dP^T of the next tile
+  // from K_n, V_n. Operand reads run two products ahead of their use, fenced
+  // so that the scheduler keeps that depth.
+  auto mphase = [&](auto DO_DQ, const __bf16* kt, const __bf16* kn, const __bf16* vn)
+      __attribute__((always_inline)) {
+    constexpr bool do_dq = decltype(DO_DQ)::value;
+    constexpr int R = 2;
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (do_dq) {
+      constexpr int NP = (BC / 16) * (D / 32);
+      auto tread = [&](int i) {  // K^T fragment of product i: key step i / (D/32), d block i % (D/32)
+        const int t = i / (D / 32), b = i % (D / 32);
+        return cat8(ld_lds_tr(kt + (tw0 ^ (32 * b)) + 16 * t * D),
+                    ld_lds_tr(kt + (tw1 ^ (32 * b)) + 16 * t * D));
+      };
+      bf16x8 ar[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) ar[j] = tread(j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int t = i / (D / 32), b = i % (D / 32);
+        acc[b] = mfma32(ar[i % R], as_bf16x8(dsf[t]), acc[b]);
+        if (i + R < NP) ar[i % R] = tread(i + R);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {
+      constexpr int NP = (D / 16) * (BC / 32);
+      auto kread = [&](int i) {
+        const int st = i / (BC / 32), kb = i % (BC / 32);
+        return ld_lds16(kn + (rw ^ (16 * st)) + 32 * kb * D);
+      };
+      auto vread = [&](int i) {
+        const int st = i / (BC / 32), kb = i % (BC / 32);
+        return ld_lds16(vn + (rw ^ (16 * st)) + 32 * kb * D);
+      };
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
         s[kb] = f32x16{};
         dp[kb] = f32x16{};
       }
-      __builtin_amdgcn_s_setprio(1);
+      bf16x8 kr[R], vr[R];
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
-          const int off = tile_off<D>(32 * kb + l32, 16 * st + 8 * hh);
-          s[kb] = mfma32(ld_lds16(&ks[buf][off]), qf[st], s[kb]);
-          dp[kb] = mfma32(ld_lds16(&vs[buf][off]), of[st], dp[kb]);
-        }
-      __builtin_amdgcn_s_setprio(0);
-
-      const int kv0 = j * BC;
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
-      u32x4 dsf[BC / 16];  // dS^T as B operands, 4 k-steps of 16 keys
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float d2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float p = fast_exp2(__builtin_fmaf(s[kb][r + u], c_log2, neg_l2));
-            if (need_mask) {
-              const int kk = kv0 + 32 * kb + 8 * ((r + u) >> 2) + 4 * hh + ((r + u) & 3);
-              if (kk >= N || (CAUSAL && kk > row)) p = 0.f;
-            }
-            d2[u] = p * (dp[kb][r + u] - dval);
-          }
-          dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16(d2[0], d2[1]);
-        }
-
-      // dQ^T += K_j^T dS^T   (M = d, N = queries, k = keys in the dS^T slot order)
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int t = 0; t < BC / 16; ++t) {
-        const int r_lo = 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
-        const int r_hi = r_lo + 8;                // slots 8hh + 4..7
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const int col = 32 * b + tr_col;
-          const bf16x8 a = cat8(ld_lds_tr(&ks[buf][tile_off<D>(r_lo, col)]),
-                                ld_lds_tr(&ks[buf][tile_off<D>(r_hi, col)]));
-          acc[b] = mfma32(a, as_bf16x8(dsf[t]), acc[b]);
-        }
+      for (int j = 0; j < R; ++j) {
+        kr[j] = kread(j);
+        vr[j] = vread(j);
       }
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int st = i / (BC / 32), kb = i % (BC / 32);
+        s[kb] = mfma32(kr[i % R], qf[st], s[kb]);
+        if (i + R < NP) kr[i % R] = kread(i + R);
+        dp[kb] = mfma32(vr[i % R], of[st], dp[kb]);
+        if (i + R < NP) vr[i % R] = vread(i + R);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
 
-    if (j + 1 < nkv) store_tile(buf ^ 1);
-    __syncthreads();
+  // Workgroup barrier without a memory fence (tile loads are waited for
+  // explicitly; the LDS reads of a phase are consumed by its own products);
+  // the fences keep every instruction on its side.
+  auto slot_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- schedule (as in the forward kernel) ---------------------------------------
+  // Group A: S_0/dP_0 in slot 0, V(t) in slot 2t+1, M(t) in slot 2t+2; group B
+  // one slot later. K_0, K_1, V_0, V_1 are loaded up front; group B issues
+  // K_{t+2} (into the buffer of K_{t-2}, last read in slot 2t-1) and V_{t+2}
+  // (into that of V_t, last read in slot 2t+1) at the start of its V(t), slot
+  // 2t+2, and waits for them at the end of its M(t), slot 2t+3; the first
+  // reader is group A's M(t+1) in slot 2t+4.
+  // Every wave runs T4 = T rounded up to 4 tiles (the barriers must match):
+  // the full work, in groups of 4, up to its last needed tile rounded up to 4
+  // (the extra tiles are fully masked, so they add nothing), then only the
+  // loads and barriers. All T4 tiles are loaded (past the sequence end they
+  // read as zeros), so no product ever reads a buffer that was never filled.
+  const int T4 = (T + 3) & ~3;
+  const int jw4 = (jw_last + 4) & ~3;
+  load_tile(eight{}, rK, wave, 0, ks0);
+  load_tile(eight{}, rV, wave, 0, vs0);
+  load_tile(eight{}, rK, wave, 1, ks1);
+  load_tile(eight{}, rV, wave, 1, vs1);
+  wait_vmem_all();
+  __syncthreads();
+  if (grp == 1) __syncthreads();
+  mphase(no{}, ks0, ks0, vs0);  // S_0, dP_0
+  slot_barrier();
+  // one tile t; P = t & 3 (static in each copy) names the buffers
+  auto tile = [&](auto P, int t) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    __bf16* const kbuf[4] = {ks0, ks1, ks2, ks3};
+    __bf16* const vbuf[2] = {vs0, vs1};
+    if (grp == 1 && t + 2 < T4) {
+      load_tile(four{}, rK, wl, t + 2, kbuf[(p + 2) & 3]);
+      load_tile(four{}, rV, wl, t + 2, vbuf[p & 1]);
+    }
+    vphase(t);
+    slot_barrier();
+    mphase(yes{}, kbuf[p], kbuf[(p + 1) & 3], vbuf[(p + 1) & 1]);
+    wait_vmem_all();  // (group A has none in flight)
+    slot_barrier();
+  };
+  using c0 = std::integral_constant<int, 0>;
+  using c1 = std::integral_constant<int, 1>;
+  using c2 = std::integral_constant<int, 2>;
+  using c3 = std::integral_constant<int, 3>;
+  int t = 0;
+  for (; t < jw4; t += 4) {
+    tile(c0{}, t);
+    tile(c1{}, t + 1);
+    tile(c2{}, t + 2);
+    tile(c3{}, t + 3);
   }
+  for (; t < T4; ++t) {
+    if (grp == 1 && t + 2 < T4) {
+      __bf16* kf = ((t + 2) & 3) == 0 ? ks0 : ((t + 2) & 3) == 1 ? ks1 : ((t + 2) & 3) == 2 ? ks2 : ks3;
+      load_tile(four{}, rK, wl, t + 2, kf);
+      load_tile(four{}, rV, wl, t + 2, (t & 1) ? vs1 : vs0);
+    }
+    slot_barrier();
+    wait_vmem_all();
+    slot_barrier();
+  }
+  if (grp == 0) slot_barrier();
 
   // ---- epilogue: dQ = scale * dQ^T, bf16 ---------------------------------------
   if (!wave_active || row >= N) return;
@@ -474,8 +599,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   using C = BwdCfg<D>;
-  constexpr int DQ_NW = D == 128 ? 8 : 4;
-  using Cq = DqCfg<D, DQ_NW>;
+  using Cq = DqCfg<D>;
   const long long rows = (long long)a.B * a.H * a.N;
   f32x2* rowstat = reinterpret_cast<f32x2*>(a.rowstat);
   const float c_log2 = a.softmax_scale * kLog2e;
@@ -499,7 +623,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   {
     const int nq = (a.N + Cq::BR - 1) / Cq::BR;
     const long long total = (long long)nq * a.B * a.H;
-    return launch_kernel(bwd_dq_kernel<D, DQ_NW, CAUSAL>, dim3((unsigned)total),
+    return launch_kernel(bwd_dq_kernel<D, CAUSAL>, dim3((unsigned)total),
                          dim3(Cq::THREADS), a.stream, (const __bf16*)a.Q, (const __bf16*)a.K,
                          (const __bf16*)a.V, (const __bf16*)a.dO, (const f32x2*)rowstat,
                          (__bf16*)a.dQ, a.N, a.B * a.H, c_log2, a.softmax_scale);
