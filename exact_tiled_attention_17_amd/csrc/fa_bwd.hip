@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// 2. Main backward kernel
+// 2. dK/dV kernel
 // ---------------------------------------------------------------------------
 template <int D>
 struct BwdCfg {
@@ -74,16 +74,21 @@ struct BwdCfg {
   static constexpr int QB = 2;              // 32-query blocks per step
   static constexpr int BRB = 32 * QB;       // queries per step
   static constexpr int CH = D / 8;          // 16-byte chunks per row
-  static constexpr int TPT = 2 * BRB * CH / THREADS;  // Q/dO tile chunks per thread
-  static_assert(TPT >= 1, "work split");
+  static constexpr int TI = BRB * CH / 64;  // direct-to-LDS instructions per Q or dO tile
+  static_assert(BRB * CH % 64 == 0, "tile loads");
 };
 
 // Each 32-key block of the workgroup is served by two waves on one SIMD:
 //   P-wave:  S = Q K^T, P = exp2(c S - LSE2), dV += P^T dO;
 //   dS-wave: dP = dO V^T, dS = P (dP - D) with P from its partner through
-//            LDS, dK += dS^T Q.
-// Splitting the dK and dV accumulators keeps each wave under 256 registers,
-// so two waves share a SIMD and one's softmax overlaps the other's products.
+//            LDS (as bf16, the precision the products use), dK += dS^T Q.
+// Splitting the dK and dV accumulators keeps each wave under 256 registers.
+// The two are pipelined one query step apart, one barrier per slot: in slot s
+//   P-wave:  dV += P_{s-1}^T dO_{s-1}; S_s; P_s (vector ALUs) -> LDS
+//   dS-wave: dS_{s-1} (vector ALUs); dK += dS_{s-1}^T Q_{s-1}; dP_s
+// so on each SIMD the products of one wave overlap the vector work of the
+// other. Q, dO tiles and row statistics of three steps are resident (s - 1,
+// s, and s + 1 being loaded straight from HBM into LDS).
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -91,12 +96,22 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const f32x2* __restrict__ rowstat, __bf16* __restrict__ dK,
                      __bf16* __restrict__ dV, int N, int BH, float c_log2, float scale) {
   using C = BwdCfg<D>;
-  constexpr int BCB = C::BCB, BRB = C::BRB, QB = C::QB, CH = C::CH;
-  static_assert(BRB <= 64, "one row statistic per lane of one wave");
-  __shared__ __attribute__((aligned(16))) __bf16 qs[2][BRB * D];         // Q tiles
-  __shared__ __attribute__((aligned(16))) __bf16 dos[2][BRB * D];        // dO tiles
-  __shared__ __attribute__((aligned(16))) f32x4 ps[C::KBLK][4 * QB][64];  // P, lane-major
-  __shared__ __attribute__((aligned(16))) f32x2 rs[2][BRB];           // (LSE2, D) per query
+  constexpr int BCB = C::BCB, BRB = C::BRB, QB = C::QB, CH = C::CH, TI = C::TI;
+  // three buffers of each kind, as separate arrays so that every access
+  // names its buffer statically; Q and dO tiles row-major, chunk c of row r at
+  // c ^ swz(r) (operand-row and transposing reads both conflict-free)
+  __shared__ __attribute__((aligned(16))) __bf16 qs0[BRB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 qs1[BRB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 qs2[BRB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 os0[BRB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 os1[BRB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 os2[BRB * D];
+  __shared__ __attribute__((aligned(16))) u32x4 ps0[C::KBLK][2 * QB][64];  // P^T operands, lane-major
+  __shared__ __attribute__((aligned(16))) u32x4 ps1[C::KBLK][2 * QB][64];
+  __shared__ __attribute__((aligned(16))) u32x4 ps2[C::KBLK][2 * QB][64];
+  __shared__ __attribute__((aligned(16))) f32x2 rs0[BRB];  // (LSE2, D) per query
+  __shared__ __attribute__((aligned(16))) f32x2 rs1[BRB];
+  __shared__ __attribute__((aligned(16))) f32x2 rs2[BRB];
 
   const int nkb = (N + BCB - 1) / BCB;
   int bh, kb;
@@ -109,10 +124,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int hh = lane >> 5;
   const bool pwave = wave < C::KBLK;           // role (wave-uniform)
   const int kblk = pwave ? wave : wave - C::KBLK;
-  // transposing-read addressing of this lane (see ld_lds_tr)
-  const int tr_grp = lane >> 4, tr_i = lane & 15;
-  const int tr_e = tr_i >> 2;                              // which k-slot row it fetches
-  const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);   // column within a 32-block
+  const int tr_i = lane & 15;
+  const int tr_e = tr_i >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -135,146 +149,206 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       frag[s] = as_bf16x8(buf_load16(rF, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
   }
 
-  // Q / dO tile loaders: P-waves load Q, dS-waves dO
-  const int tl = tid % (C::THREADS / 2);
-  const auto rT = pwave ? rQ : rdO;
-  u32x4 stg[C::TPT];
-  f32x2 rstg = {0.f, 0.f};
-  auto load_q = [&](int i) {
-    const int q0 = i * BRB;
-#pragma unroll
-    for (int r = 0; r < C::TPT; ++r) {
-      const int j = tl + r * (C::THREADS / 2);
-      stg[r] = buf_load16(rT, (uint32_t)(q0 + j / CH) * (D * 2) + (j % CH) * 16);
-    }
-    if (wave == C::NW - 1)
-      rstg = __builtin_bit_cast(
-          f32x2, __builtin_amdgcn_raw_buffer_load_b64(rRS, (uint32_t)(q0 + lane) * 8u, 0, 0));
+  // ---- step loads, straight from HBM into LDS: the Q and dO tiles of 64
+  // queries (instruction n fills chunk positions [64 n, 64 n + 64), dealt
+  // round-robin over the 8 waves) and the 64 row statistics (wave 0) -------
+  auto src = [&](int n) -> uint32_t {
+    const int p = 64 * n + lane;
+    const int r = p / CH, pc = p % CH;
+    return (uint32_t)(r * (D * 2) + ((pc ^ swz<D>(r)) * 16));
   };
-  auto store_q = [&](int i, int buf) {
-    __bf16* t = pwave ? qs[buf] : dos[buf];
+  constexpr int LM = (TI + 7) / 8;
+  uint32_t src_w[LM];
 #pragma unroll
-    for (int r = 0; r < C::TPT; ++r) {
-      const int j = tl + r * (C::THREADS / 2);
-      st_lds16(&t[tile_off<D>(j / CH, 8 * (j % CH))], stg[r]);
-    }
-    // rows past the end get LSE2 = +inf and D = 0, so their P and dS are 0
-    if (wave == C::NW - 1 && lane < BRB)
-      rs[buf][lane] = i * BRB + lane < N ? rstg : f32x2{INFINITY, 0.f};
-  };
-
-  // this wave's accumulator: dV (P-wave) or dK (dS-wave), M = keys, N = d
-  f32x16 acc_kd[D / 32];
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) acc_kd[b] = f32x16{};
-
+  for (int m = 0; m < LM; ++m) src_w[m] = src(wave + 8 * m);
   const int nqt = (N + BRB - 1) / BRB;
-  const int i0 = CAUSAL ? k0 / BRB : 0;
-  const int nsteps = nqt - i0;
-
-  load_q(i0);
-  store_q(i0, 0);
-  wait_vmem_all();
-  __syncthreads();
-
-  for (int it = 0; it < nsteps; ++it) {
-    const int i = i0 + it;
-    const int cur = it & 1;
-    const int q0 = i * BRB;
-    if (it + 1 < nsteps) load_q(i + 1);
-    // first product: S = Q K^T (P-wave) or dP = dO V^T (dS-wave), one per
-    // 32-query block; M = 32 queries, N = this block's 32 keys; lane = one
-    // key, 16 queries
-    f32x16 sd[QB];
-    {
-      const __bf16* a_tile = pwave ? qs[cur] : dos[cur];
+  const int i0 = CAUSAL ? k0 / BRB : 0;  // first query tile that sees the block's keys
+  auto load_step = [&](int s, __bf16* qd, __bf16* od, f32x2* rsd) __attribute__((always_inline)) {
+    const int q0 = (i0 + s) * BRB;
+    const uint32_t row0 = (uint32_t)q0 * (D * 2);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sd[qb] = mfma32(ld_lds16(&a_tile[tile_off<D>(32 * qb + l32, 16 * st + 8 * hh)]),
-                          frag[st], sd[qb]);
-      __builtin_amdgcn_s_setprio(0);
-    }
-
-    u32x4 opnd[QB][2];  // P^T (P-wave) or dS^T (dS-wave) as A operands, 2 k-steps each
-    if (pwave) {
-      // P = exp2(c S - LSE2); hand P (float32, lane-major) to the dS-wave
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qb0 = q0 + 32 * qb;
-        const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (kw0 + 32 > N);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int m0 = 32 * qb + 8 * g + 4 * hh;
-          const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
-          const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
-          const float l2v[4] = {st01[0], st01[2], st23[0], st23[2]};
-          f32x4 p;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pv = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l2v[e]));
-            if (need_mask) {
-              const int q = q0 + m0 + e;
-              if (key >= N || (CAUSAL && key > q)) pv = 0.f;
-            }
-            p[e] = pv;
-          }
-          ps[kblk][4 * qb + g][lane] = p;
-          // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
-          opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
-          opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
-        }
+    for (int m = 0; m < LM; ++m) {
+      const int n = wave + 8 * m;
+      if (n < TI) {
+        buf_load16_lds(rQ, src_w[m], row0, qd + 64 * n * 8);
+        buf_load16_lds(rdO, src_w[m], row0, od + 64 * n * 8);
       }
     }
-    __syncthreads();  // P handed over
-    if (!pwave) {
-      // dS = P (dP - D)
+    if (wave == 0) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int m0 = 32 * qb + 8 * g + 4 * hh;
-          const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rs[cur][m0]);
-          const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rs[cur][m0 + 2]);
-          const float dvv[4] = {st01[1], st01[3], st23[1], st23[3]};
-          const f32x4 p = ps[kblk][4 * qb + g][lane];
-          float ds[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[qb][4 * g + e] - dvv[e]);
-          opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(ds[0], ds[1]);
-          opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(ds[2], ds[3]);
-        }
+      for (int n = 0; n < 2; ++n)
+        buf_load4_lds(rRS, 4u * lane, (uint32_t)q0 * 8u + 256u * n,
+                      reinterpret_cast<char*>(rsd) + 256 * n);
     }
+  };
 
-    // second product: dV += P^T dO (P-wave) or dK += dS^T Q (dS-wave);
-    // M = keys, N = d, k = queries; the B operand is read transposed from the
-    // row-major tile, rows in the A operand's slot order
-    {
-      const __bf16* b_tile = pwave ? dos[cur] : qs[cur];
-      __builtin_amdgcn_s_setprio(1);
+  // ---- LDS read offsets (elements): operand rows (row 32 qb + l32, chunk
+  // 2 st + hh) at rw ^ 16 st (+ 32 qb D); transposing reads (rows
+  // 32 qb + 16 t + 4 hh + tr_e and that + 8, column 32 b + tr_col) at
+  // tw ^ 32 b (+ (32 qb + 16 t) D) -------------------------------------------
+  int rw = tile_off<D>(l32, 8 * hh);
+  int tw0 = tile_off<D>(4 * hh + tr_e, tr_col);
+  int tw1 = tile_off<D>(4 * hh + tr_e + 8, tr_col);
+  asm volatile("" : "+v"(rw), "+v"(tw0), "+v"(tw1));
+
+  f32x16 acc_kd[D / 32];  // dV (P-wave) or dK (dS-wave): M = keys, N = d
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) acc_kd[b] = f32x16{};
+  f32x16 sd[QB];      // S (P-wave) or dP (dS-wave) of a step: lane = one key, 16 queries
+  u32x4 opnd[QB][2];  // P^T (P-wave) or dS^T (dS-wave) as A operands, 2 k-steps each
+
+  // sd = (Q or dO tile rows) x frag^T, one product per 32-query block
+  auto first_product = [&](const __bf16* tile) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
+        sd[qb] = mfma32(ld_lds16(tile + (rw ^ (16 * st)) + 32 * qb * D), frag[st], sd[qb]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // acc_kd += opnd^T (dO or Q tile): M = keys, N = d, k = queries; the B
+  // operand is read transposed, rows in the A operand's slot order
+  auto second_product = [&](const __bf16* tile) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r_lo = 32 * qb + 16 * t + 4 * hh + tr_e;  // slots 8hh + 0..3
-          const int r_hi = r_lo + 8;                          // slots 8hh + 4..7
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int b = 0; b < D / 32; ++b) {
-            const int col = 32 * b + tr_col;
-            const bf16x8 bb = cat8(ld_lds_tr(&b_tile[tile_off<D>(r_lo, col)]),
-                                   ld_lds_tr(&b_tile[tile_off<D>(r_hi, col)]));
-            acc_kd[b] = mfma32(as_bf16x8(opnd[qb][t]), bb, acc_kd[b]);
-          }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          const __bf16* base = tile + (32 * qb + 16 * t) * D;
+          const bf16x8 bb = cat8(ld_lds_tr(base + (tw0 ^ (32 * b))), ld_lds_tr(base + (tw1 ^ (32 * b))));
+          acc_kd[b] = mfma32(as_bf16x8(opnd[qb][t]), bb, acc_kd[b]);
         }
-      __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // query q0 + m (m = 32 qb + 8 g + 4 hh + e) contributes to this lane's key
+  // iff (unsigned)(m + mbase) < mbound: the query exists and, if causal, is at
+  // or after the key; a key past the end contributes nothing
+  auto mask_bounds = [&](int q0, int& mbase, unsigned& mbound) __attribute__((always_inline)) {
+    const int qlo = CAUSAL ? key : 0;
+    mbase = q0 - qlo;
+    mbound = key < N ? (unsigned)(N - qlo) : 0u;
+  };
+  // P-wave: P = exp2(c S - LSE2) -> opnd (bf16) and to LDS for the partner
+  auto p_phase = [&](int s, const f32x2* rsb, u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
+    const int q0 = (i0 + s) * BRB;
+    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + BRB > N);
+    int mbase;
+    unsigned mbound;
+    mask_bounds(q0, mbase, mbound);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m0 = 32 * qb + 8 * g + 4 * hh;
+        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rsb[m0]);
+        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rsb[m0 + 2]);
+        const float l2v[4] = {st01[0], st01[2], st23[0], st23[2]};
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l2v[e]));
+          if (need_mask && (unsigned)(m0 + e + mbase) >= mbound) p[e] = 0.f;
+        }
+        // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
+        opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
+        opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
+      }
+#pragma unroll
+    for (int j = 0; j < 2 * QB; ++j) psb[kblk][j][lane] = opnd[j >> 1][j & 1];
+  };
+  // dS-wave: dS = P (dP - D) -> opnd (bf16)
+  auto ds_phase = [&](const f32x2* rsb, const u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
+    u32x4 pp[2 * QB];
+#pragma unroll
+    for (int j = 0; j < 2 * QB; ++j) pp[j] = psb[kblk][j][lane];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m0 = 32 * qb + 8 * g + 4 * hh;
+        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rsb[m0]);
+        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rsb[m0 + 2]);
+        const float dvv[4] = {st01[1], st01[3], st23[1], st23[3]};
+        const uint32_t w0 = pp[2 * qb + (g >> 1)][2 * (g & 1)];
+        const uint32_t w1 = pp[2 * qb + (g >> 1)][2 * (g & 1) + 1];
+        const float p[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
+                            __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
+        float ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[qb][4 * g + e] - dvv[e]);
+        opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(ds[0], ds[1]);
+        opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(ds[2], ds[3]);
+      }
+  };
+
+  auto slot_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- schedule ------------------------------------------------------------------
+  // Slot 0 has only step 0's first half, the last slot only the last step's
+  // second half. The middle slots run in groups of three (buffer index
+  // s mod 3, static in each copy); their count is padded to a multiple of 3
+  // with steps past the end of the sequence, whose queries are all masked.
+  const int nsteps = nqt - i0;
+  const int last = 3 * ((nsteps + 1) / 3) + 1;  // >= nsteps, == 1 (mod 3)
+  __bf16* const qbuf[3] = {qs0, qs1, qs2};
+  __bf16* const obuf[3] = {os0, os1, os2};
+  u32x4 (*const pbuf[3])[2 * QB][64] = {ps0, ps1, ps2};
+  f32x2* const rbuf[3] = {rs0, rs1, rs2};
+  // ROLE: P-wave (true) or dS-wave; each role runs its own straight-line copy
+  // of the schedule (same barriers), so neither carries the other's registers
+  auto slot = [&](auto ROLE, auto B3, auto HAS_PREV, auto HAS_CUR, int s) __attribute__((always_inline)) {
+    constexpr bool p_role = decltype(ROLE)::value;
+    constexpr int b = decltype(B3)::value, bp = (b + 2) % 3, bn = (b + 1) % 3;
+    constexpr bool has_prev = decltype(HAS_PREV)::value, has_cur = decltype(HAS_CUR)::value;
+    if constexpr (has_cur)
+      if (s + 1 < last) load_step(s + 1, qbuf[bn], obuf[bn], rbuf[bn]);
+    if constexpr (p_role) {
+      if constexpr (has_prev) second_product(obuf[bp]);  // dV += P_{s-1}^T dO_{s-1}
+      if constexpr (has_cur) {
+        first_product(qbuf[b]);                           // S_s
+        p_phase(s, rbuf[b], pbuf[b]);                     // P_s
+      }
+    } else {
+      if constexpr (has_prev) {
+        ds_phase(rbuf[bp], pbuf[bp]);                     // dS_{s-1}
+        second_product(qbuf[bp]);                         // dK += dS_{s-1}^T Q_{s-1}
+      }
+      if constexpr (has_cur) first_product(obuf[b]);     // dP_s
     }
-    if (it + 1 < nsteps) store_q(i + 1, cur ^ 1);
-    __syncthreads();
-  }
+    wait_vmem_all();  // the loads of step s + 1 have landed
+    slot_barrier();
+  };
+  using c0 = std::integral_constant<int, 0>;
+  using c1 = std::integral_constant<int, 1>;
+  using c2 = std::integral_constant<int, 2>;
+  using yes = std::true_type;
+  using no = std::false_type;
+  auto run = [&](auto ROLE) __attribute__((always_inline)) {
+    slot(ROLE, c0{}, no{}, yes{}, 0);
+    for (int s = 1; s < last; s += 3) {
+      slot(ROLE, c1{}, yes{}, yes{}, s);
+      slot(ROLE, c2{}, yes{}, yes{}, s + 1);
+      slot(ROLE, c0{}, yes{}, yes{}, s + 2);
+    }
+    slot(ROLE, c1{}, yes{}, no{}, last);
+  };
+
+  load_step(0, qs0, os0, rs0);
+  wait_vmem_all();
+  __syncthreads();
+  if (pwave)
+    run(yes{});
+  else
+    run(no{});
 
   // ---- epilogue: dV = dV_acc (P-waves), dK = scale * dK_acc (dS-waves), bf16 --
   __bf16* out = pwave ? dV : dK;

@@ -78,6 +78,14 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_
                                            voff, soff, 0, 0);
 }
 
+// 4 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds_base + 4 l.
+__device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
+                                           voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
