@@ -42,7 +42,7 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
                                                      const __bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE,
-                                                     f32x2* __restrict__ rowstat, long long rows) {
+                                                     float* __restrict__ rowstat, long long rows) {
   constexpr int CH = D / 8;  // lanes per row
   const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long row = gt / CH;
@@ -59,7 +59,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   }
 #pragma unroll
   for (int off = CH / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, CH);
-  if (row < rows && c == 0) rowstat[row] = f32x2{LSE[row] * kLog2e, acc};
+  if (row < rows && c == 0) {
+    rowstat[row] = LSE[row] * kLog2e;  // LSE in base 2
+    rowstat[rows + row] = acc;         // D
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -93,7 +96,7 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                     const f32x2* __restrict__ rowstat, __bf16* __restrict__ dK,
+                     const float* __restrict__ rowstat, __bf16* __restrict__ dK,
                      __bf16* __restrict__ dV, int N, int BH, float c_log2, float scale) {
   using C = BwdCfg<D>;
   constexpr int BCB = C::BCB, BRB = C::BRB, QB = C::QB, CH = C::CH, TI = C::TI;
@@ -109,9 +112,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) u32x4 ps0[C::KBLK][2 * QB][64];  // P^T operands, lane-major
   __shared__ __attribute__((aligned(16))) u32x4 ps1[C::KBLK][2 * QB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ps2[C::KBLK][2 * QB][64];
-  __shared__ __attribute__((aligned(16))) f32x2 rs0[BRB];  // (LSE2, D) per query
-  __shared__ __attribute__((aligned(16))) f32x2 rs1[BRB];
-  __shared__ __attribute__((aligned(16))) f32x2 rs2[BRB];
+  __shared__ __attribute__((aligned(16))) float rs0[2 * BRB];  // LSE2 of the step's queries, then D
+  __shared__ __attribute__((aligned(16))) float rs1[2 * BRB];
+  __shared__ __attribute__((aligned(16))) float rs2[2 * BRB];
 
   const int nkb = (N + BCB - 1) / BCB;
   int bh, kb;
@@ -134,7 +137,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rK = make_rsrc(K + head, head_bytes);
   const auto rV = make_rsrc(V + head, head_bytes);
   const auto rdO = make_rsrc(dO + head, head_bytes);
-  const auto rRS = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 8u);
+  // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
+  const auto rL2 = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rDD = make_rsrc(rowstat + (size_t)BH * N + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int k0 = kb * BCB;
   const int kw0 = k0 + 32 * kblk;  // this wave's first key
@@ -163,7 +168,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int m = 0; m < LM; ++m) src_w[m] = src(wave + 8 * m);
   const int nqt = (N + BRB - 1) / BRB;
   const int i0 = CAUSAL ? k0 / BRB : 0;  // first query tile that sees the block's keys
-  auto load_step = [&](int s, __bf16* qd, __bf16* od, f32x2* rsd) __attribute__((always_inline)) {
+  auto load_step = [&](int s, __bf16* qd, __bf16* od, float* rsd) __attribute__((always_inline)) {
     const int q0 = (i0 + s) * BRB;
     const uint32_t row0 = (uint32_t)q0 * (D * 2);
 #pragma unroll
@@ -175,10 +180,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       }
     }
     if (wave == 0) {
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        buf_load4_lds(rRS, 4u * lane, (uint32_t)q0 * 8u + 256u * n,
-                      reinterpret_cast<char*>(rsd) + 256 * n);
+      buf_load4_lds(rL2, 4u * lane, (uint32_t)q0 * 4u, rsd);
+      buf_load4_lds(rDD, 4u * lane, (uint32_t)q0 * 4u, rsd + BRB);
     }
   };
 
@@ -197,32 +200,50 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   f32x16 sd[QB];      // S (P-wave) or dP (dS-wave) of a step: lane = one key, 16 queries
   u32x4 opnd[QB][2];  // P^T (P-wave) or dS^T (dS-wave) as A operands, 2 k-steps each
 
-  // sd = (Q or dO tile rows) x frag^T, one product per 32-query block
+  // sd = (Q or dO tile rows) x frag^T, one product per 32-query block. In both
+  // products the operand reads run R products ahead of their use, fenced so
+  // that the scheduler keeps that depth.
+  constexpr int R = 2;
   auto first_product = [&](const __bf16* tile) __attribute__((always_inline)) {
+    constexpr int NP = (D / 16) * QB;  // product i: k-step i / QB, query block i % QB
+    auto rd = [&](int i) { return ld_lds16(tile + (rw ^ (16 * (i / QB))) + 32 * (i % QB) * D); };
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
+    bf16x8 ar[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) ar[j] = rd(j);
     __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        sd[qb] = mfma32(ld_lds16(tile + (rw ^ (16 * st)) + 32 * qb * D), frag[st], sd[qb]);
+    for (int i = 0; i < NP; ++i) {
+      sd[i % QB] = mfma32(ar[i % R], frag[i / QB], sd[i % QB]);
+      if (i + R < NP) ar[i % R] = rd(i + R);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // acc_kd += opnd^T (dO or Q tile): M = keys, N = d, k = queries; the B
   // operand is read transposed, rows in the A operand's slot order
   auto second_product = [&](const __bf16* tile) __attribute__((always_inline)) {
+    constexpr int NB = D / 32;
+    constexpr int NP = QB * 2 * NB;  // product i: k-step i / NB (= 2 qb + t), d block i % NB
+    auto rd = [&](int i) {
+      const __bf16* base = tile + 16 * (i / NB) * D;
+      const int b = i % NB;
+      return cat8(ld_lds_tr(base + (tw0 ^ (32 * b))), ld_lds_tr(base + (tw1 ^ (32 * b))));
+    };
+    bf16x8 br[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) br[j] = rd(j);
     __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const __bf16* base = tile + (32 * qb + 16 * t) * D;
-          const bf16x8 bb = cat8(ld_lds_tr(base + (tw0 ^ (32 * b))), ld_lds_tr(base + (tw1 ^ (32 * b))));
-          acc_kd[b] = mfma32(as_bf16x8(opnd[qb][t]), bb, acc_kd[b]);
-        }
+    for (int i = 0; i < NP; ++i) {
+      const int ks = i / NB;
+      acc_kd[i % NB] = mfma32(as_bf16x8(opnd[ks >> 1][ks & 1]), br[i % R], acc_kd[i % NB]);
+      if (i + R < NP) br[i % R] = rd(i + R);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // query q0 + m (m = 32 qb + 8 g + 4 hh + e) contributes to this lane's key
@@ -234,24 +255,26 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     mbound = key < N ? (unsigned)(N - qlo) : 0u;
   };
   // P-wave: P = exp2(c S - LSE2) -> opnd (bf16) and to LDS for the partner
-  auto p_phase = [&](int s, const f32x2* rsb, u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
+  auto p_phase = [&](int s, const float* rsb, u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
     const int q0 = (i0 + s) * BRB;
     const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + BRB > N);
     int mbase;
     unsigned mbound;
     mask_bounds(q0, mbase, mbound);
+    f32x4 l4[QB][4];  // LSE2 of queries 32 qb + 8 g + 4 hh + 0..3, all read up front
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) l4[qb][g] = *reinterpret_cast<const f32x4*>(&rsb[32 * qb + 8 * g + 4 * hh]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int m0 = 32 * qb + 8 * g + 4 * hh;
-        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rsb[m0]);
-        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rsb[m0 + 2]);
-        const float l2v[4] = {st01[0], st01[2], st23[0], st23[2]};
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l2v[e]));
+          p[e] = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l4[qb][g][e]));
           if (need_mask && (unsigned)(m0 + e + mbase) >= mbound) p[e] = 0.f;
         }
         // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
@@ -262,25 +285,27 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int j = 0; j < 2 * QB; ++j) psb[kblk][j][lane] = opnd[j >> 1][j & 1];
   };
   // dS-wave: dS = P (dP - D) -> opnd (bf16)
-  auto ds_phase = [&](const f32x2* rsb, const u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
+  auto ds_phase = [&](const float* rsb, const u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
     u32x4 pp[2 * QB];
 #pragma unroll
     for (int j = 0; j < 2 * QB; ++j) pp[j] = psb[kblk][j][lane];
+    f32x4 d4[QB][4];  // D of queries 32 qb + 8 g + 4 hh + 0..3
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        d4[qb][g] = *reinterpret_cast<const f32x4*>(&rsb[BRB + 32 * qb + 8 * g + 4 * hh]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int m0 = 32 * qb + 8 * g + 4 * hh;
-        const f32x4 st01 = *reinterpret_cast<const f32x4*>(&rsb[m0]);
-        const f32x4 st23 = *reinterpret_cast<const f32x4*>(&rsb[m0 + 2]);
-        const float dvv[4] = {st01[1], st01[3], st23[1], st23[3]};
         const uint32_t w0 = pp[2 * qb + (g >> 1)][2 * (g & 1)];
         const uint32_t w1 = pp[2 * qb + (g >> 1)][2 * (g & 1) + 1];
         const float p[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
                             __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
         float ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[qb][4 * g + e] - dvv[e]);
+        for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[qb][4 * g + e] - d4[qb][g][e]);
         opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(ds[0], ds[1]);
         opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(ds[2], ds[3]);
       }
@@ -302,7 +327,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __bf16* const qbuf[3] = {qs0, qs1, qs2};
   __bf16* const obuf[3] = {os0, os1, os2};
   u32x4 (*const pbuf[3])[2 * QB][64] = {ps0, ps1, ps2};
-  f32x2* const rbuf[3] = {rs0, rs1, rs2};
+  float* const rbuf[3] = {rs0, rs1, rs2};
   // ROLE: P-wave (true) or dS-wave; each role runs its own straight-line copy
   // of the schedule (same barriers), so neither carries the other's registers
   auto slot = [&](auto ROLE, auto B3, auto HAS_PREV, auto HAS_CUR, int s) __attribute__((always_inline)) {
@@ -396,7 +421,7 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                   const f32x2* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
+                   const float* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
                    float c_log2, float scale) {
   using C = DqCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, CH = C::CH, TI = C::TI;
@@ -433,7 +458,9 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rK = make_rsrc(K + head, head_bytes);
   const auto rV = make_rsrc(V + head, head_bytes);
   const auto rdO = make_rsrc(dO + head, head_bytes);
-  const auto rRS = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 8u);
+  // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
+  const auto rL2 = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rDD = make_rsrc(rowstat + (size_t)BH * N + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * rblk;
@@ -453,9 +480,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     qf[s] = as_bf16x8(buf_load16(rQ, off));
     of[s] = as_bf16x8(buf_load16(rdO, off));
   }
-  const f32x2 rst = __builtin_bit_cast(
-      f32x2, __builtin_amdgcn_raw_buffer_load_b64(rRS, (uint32_t)row * 8u, 0, 0));
-  const float neg_l2 = -rst[0], dval = rst[1];
+  const float neg_l2 = -__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL2, (uint32_t)row * 4u, 0, 0));
+  const float dval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rDD, (uint32_t)row * 4u, 0, 0));
 
   // ---- tile loads, straight from HBM into LDS: instruction n of a tile fills
   // chunk positions [64 n, 64 n + 64); each lane fetches the chunk the layout
@@ -675,7 +701,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   using C = BwdCfg<D>;
   using Cq = DqCfg<D>;
   const long long rows = (long long)a.B * a.H * a.N;
-  f32x2* rowstat = reinterpret_cast<f32x2*>(a.rowstat);
+  float* rowstat = a.rowstat;
   const float c_log2 = a.softmax_scale * kLog2e;
   {
     const long long threads = rows * (D / 8);
@@ -690,7 +716,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     const hipError_t e = launch_kernel(
         bwd_dkdv_kernel<D, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
-        (const f32x2*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, c_log2,
+        (const float*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, c_log2,
         a.softmax_scale);
     if (e != hipSuccess) return e;
   }
@@ -699,7 +725,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     const long long total = (long long)nq * a.B * a.H;
     return launch_kernel(bwd_dq_kernel<D, CAUSAL>, dim3((unsigned)total),
                          dim3(Cq::THREADS), a.stream, (const __bf16*)a.Q, (const __bf16*)a.K,
-                         (const __bf16*)a.V, (const __bf16*)a.dO, (const f32x2*)rowstat,
+                         (const __bf16*)a.V, (const __bf16*)a.dO, (const float*)rowstat,
                          (__bf16*)a.dQ, a.N, a.B * a.H, c_log2, a.softmax_scale);
   }
 }

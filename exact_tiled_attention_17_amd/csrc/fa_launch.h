@@ -32,7 +32,7 @@ struct BwdArgs {
   bool causal;
   float softmax_scale;
   hipStream_t stream;
-  float* rowstat; // [B,H,N] x 2 float32 scratch: (LSE in base 2, D = dO . O)
+  float* rowstat; // 2 x [B,H,N] float32 scratch: LSE in base 2 for every row, then D = dO . O
 };
 
 // Enqueues `kernel` and returns the status of this launch alone (not the
