@@ -273,9 +273,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const int m0 = 32 * qb + 8 * g + 4 * hh;
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l4[qb][g][e]));
-          if (need_mask && (unsigned)(m0 + e + mbase) >= mbound) p[e] = 0.f;
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l4[qb][g][e]));
+        if (need_mask) {  // selects under one wave-uniform branch
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = (unsigned)(m0 + e + mbase) >= mbound ? 0.f : p[e];
         }
         // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
         opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
@@ -541,8 +542,11 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int u2 = 0; u2 < 2; ++u2) {
           const float p = fast_exp2(__builtin_fmaf(s[kb][r + u2], c_log2, neg_l2));
           d2[u2] = p * (dp[kb][r + u2] - dval);
-          // dS itself is zeroed: a masked tile may hold stale data
-          if (need_mask && 32 * kb + 8 * ((r + u2) >> 2) + ((r + u2) & 3) > lim) d2[u2] = 0.f;
+        }
+        if (need_mask) {  // dS itself is zeroed: a masked tile may hold stale data
+#pragma unroll
+          for (int u2 = 0; u2 < 2; ++u2)
+            d2[u2] = 32 * kb + 8 * ((r + u2) >> 2) + ((r + u2) & 3) > lim ? 0.f : d2[u2];
         }
         dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16(d2[0], d2[1]);
       }
