@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -38,13 +39,22 @@ PAGE_TIMES_MS = {"2x8x512x64": 0.85, "4x32x1024x128": 2.1, "8x64x2048x128": 8.3,
                  "4x64x4096x128": 15.2}
 
 
+def _strip_comments(src: str) -> str:
+    """C++ source without comments and blank lines (string literals in these
+    sources hold no comment markers)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources, to tell whether stored counters still apply."""
+    """sha256 over the HIP sources' code (comments dropped), to tell whether
+    stored counters still apply."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

@@ -5,20 +5,22 @@
 // backward file). Three launches on one stream:
 //
 //  1. bwd_pre_kernel: per query row, D_i = dO_i . O_i (float32) and the LSE in
-//     base 2.
+//     base 2, as two planes.
 //  2. bwd_dkdv_kernel: one workgroup per (batch, head, block of 128 keys); each
 //     32-key block has a P-wave (dV) and a dS-wave (dK) on one SIMD, holding
-//     float32 accumulators for the whole sweep over query tiles of 64 rows.
-//     The Q, dO tiles sit row-major in LDS; operands that need them transposed
-//     use gfx950's transposing LDS read instead of a second, transposed copy.
-//     Per query tile, on 32x32x16 bf16 matrix cores:
+//     float32 accumulators for the whole sweep over query tiles of 64 rows,
+//     pipelined one query step apart. The Q, dO tiles sit row-major in LDS;
+//     operands that need them transposed use gfx950's transposing LDS read
+//     instead of a second, transposed copy. Per query tile, on 32x32x16 bf16
+//     matrix cores:
 //        S = Q K^T, dP = dO V^T        (lane = one key, 16 queries)
 //        P = exp2(c S - LSE2), dS = P (dP - D)
 //        dV += P^T dO, dK += dS^T Q    (P^T, dS^T straight from registers)
 //     Causal: query tiles that see none of the block's keys are skipped.
 //  3. bwd_dq_kernel: one workgroup per (batch, head, query tile), sweeping key
-//     tiles like the forward: S and dP are recomputed and dQ += dS K is summed
-//     in registers, so dQ needs no atomics and no float32 scratch.
+//     tiles like the forward (and with its two-group schedule): S and dP are
+//     recomputed and dQ += dS K is summed in registers, so dQ needs no atomics
+//     and no float32 scratch.
 //
 // The pages' backward gathers dQ with atomic updates ("RTX Flash Attention
 // Implementation COMPLETE", CUDA Kernel Design, backward kernel); on MI355X the

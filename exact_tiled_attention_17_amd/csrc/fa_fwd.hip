@@ -200,13 +200,14 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int kv0 = u * BC;
     const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
     if (need_mask) {
+      // key kv0 + 32 kb + 8 (r / 4) + 4 hh + r % 4 is masked iff its offset
+      // 32 kb + 8 (r / 4) + r % 4 exceeds lim (one compare with a constant)
+      const int lim = (CAUSAL ? min(row, N - 1) : N - 1) - kv0 - 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= N || (CAUSAL && key > row)) sacc[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : sacc[kb][r];
     }
     float mx = -INFINITY;
 #pragma unroll
