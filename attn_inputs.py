@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for exact attention, as bf16 bit patterns.
+"""Seeded synthetic inputs for exact attention, as 16-bit bit patterns.
 
 This module is shared by the CPU oracle's tests and by the GPU path's tests
 and benchmark. It holds no attention arithmetic: it only draws i.i.d. normal
@@ -7,7 +7,8 @@ samples and rounds them to bfloat16, so that both sides see identical bits.
 Recipe (the same for every workload):
   * generator: ``numpy.random.default_rng(seed)`` (PCG64);
   * each tensor: ``standard_normal(shape, float32) * sigma``, then
-    round-to-nearest-even to bfloat16, kept as ``uint16`` bit patterns;
+    round-to-nearest-even to bfloat16 (or, when asked, to IEEE binary16),
+    kept as ``uint16`` bit patterns;
   * draw order: Q, K, V, then dO (only when gradients are wanted).
 
 The five workloads are the shapes the "RTX Flash Attention Implementation
@@ -73,6 +74,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy's conversion: round to
+    nearest, ties to even; overflow to infinity) and return the uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def normal_bf16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
     """One tensor of N(0, sigma^2) samples rounded to bf16 (uint16 bits)."""
     x = rng.standard_normal(shape, dtype=np.float32)
@@ -81,18 +88,30 @@ def normal_bf16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
     return f32_to_bf16_bits(x)
 
 
+def normal_f16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    """One tensor of N(0, sigma^2) samples rounded to binary16 (uint16 bits)."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return f32_to_f16_bits(x)
+
+
 def make_qkv(B: int, H: int, N: int, d: int, seed: int, *, sigma_qk: float = 1.0,
-             sigma_v: float = 1.0, with_do: bool = False) -> dict:
-    """Q, K, V (and dO) of shape [B, H, N, d] as bf16 bit patterns."""
+             sigma_v: float = 1.0, with_do: bool = False, dtype: str = "bf16") -> dict:
+    """Q, K, V (and dO) of shape [B, H, N, d] as 16-bit patterns: bf16 by
+    default, IEEE binary16 with dtype="f16" (same draws, other rounding)."""
+    if dtype not in ("bf16", "f16"):
+        raise ValueError(f"dtype must be 'bf16' or 'f16', got {dtype!r}")
+    normal = normal_bf16 if dtype == "bf16" else normal_f16
     rng = np.random.default_rng(seed)
     shape = (B, H, N, d)
     out = {
-        "q": normal_bf16(rng, shape, sigma_qk),
-        "k": normal_bf16(rng, shape, sigma_qk),
-        "v": normal_bf16(rng, shape, sigma_v),
+        "q": normal(rng, shape, sigma_qk),
+        "k": normal(rng, shape, sigma_qk),
+        "v": normal(rng, shape, sigma_v),
     }
     if with_do:
-        out["do"] = normal_bf16(rng, shape, sigma_v)
+        out["do"] = normal(rng, shape, sigma_v)
     return out
 
 

@@ -1,8 +1,8 @@
 """Exact tiled attention for AMD Instinct MI355X (gfx950).
 
 A thin binding of ``libfa.so`` (C ABI in ``include/fa.h``). The functions
-``fa_fwd``, ``fa_bwd`` and ``fa_status_string`` mirror the C entry points one
-to one (raw device pointers as Python ints, ``stream`` as a hipStream_t
+``fa_fwd``, ``fa_bwd``, ``fa_fwd_ex``, ``fa_bwd_ex`` and ``fa_status_string``
+mirror the C entry points one to one (raw device pointers as Python ints, ``stream`` as a hipStream_t
 handle). ``forward`` and ``backward`` are conveniences over torch tensors:
 they check dtypes and shapes, allocate outputs with torch and pass
 ``data_ptr()`` and the current stream; every step of the computation runs in
@@ -10,8 +10,8 @@ the library's HIP kernels. There is no fallback: if the library is missing
 or cannot be loaded, every call raises.
 
 Tensor layout is [batch, heads, seq_len, head_dim] as on "RTX Flash Attention
-Implementation COMPLETE" (Usage Examples), bf16, contiguous; the LSE is
-float32 [batch, heads, seq_len].
+Implementation COMPLETE" (Usage Examples), bf16 or float16 (the page's Mixed
+Precision feature), contiguous; the LSE is float32 [batch, heads, seq_len].
 """
 from __future__ import annotations
 
@@ -19,8 +19,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_status_string", "fa_last_hip_error", "forward", "backward", "load",
-           "FAError", "LIB_PATH"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_status_string", "fa_last_hip_error",
+           "forward", "backward", "load", "FAError", "LIB_PATH", "FA_DTYPE_BF16", "FA_DTYPE_F16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -29,6 +29,9 @@ FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 FA_ERR_OUT_OF_MEMORY = 4
+
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F16 = 1
 
 _lib = None
 
@@ -64,6 +67,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fa_fwd.restype = ci
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
     lib.fa_bwd.restype = ci
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.fa_fwd_ex.restype = ci
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.fa_bwd_ex.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -92,6 +99,28 @@ def fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal, softmax_scale, s
                          float(softmax_scale), stream or None)
 
 
+def fa_fwd_ex(Q, K, V, O, LSE, B, H, N, d, causal, softmax_scale, dtype, stream) -> int:
+    """C ``fa_fwd_ex``: as ``fa_fwd`` with the element type (FA_DTYPE_*)."""
+    return load().fa_fwd_ex(Q, K, V, O, LSE or None, B, H, N, d, int(causal),
+                            float(softmax_scale), int(dtype), stream or None)
+
+
+def fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal, softmax_scale, dtype,
+              stream) -> int:
+    """C ``fa_bwd_ex``: as ``fa_bwd`` with the element type (FA_DTYPE_*)."""
+    return load().fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, int(causal),
+                            float(softmax_scale), int(dtype), stream or None)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
+    raise TypeError(f"tensors must be bfloat16 or float16, got {t.dtype}")
+
+
 def _check(name, t, shape, dtype, device):
     import torch
     if not isinstance(t, torch.Tensor):
@@ -112,28 +141,29 @@ def _scale(scale, d):
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, *, out=None, lse=None,
             need_lse: bool = True):
-    """O, LSE = attention(q, k, v). q, k, v: bf16 [B, H, N, d] on one GPU."""
+    """O, LSE = attention(q, k, v). q, k, v: bf16 or float16 [B, H, N, d] on one GPU."""
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [batch, heads, seq_len, head_dim]")
     B, H, N, d = q.shape
     dev = q.device
+    code = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(name, t, (B, H, N, d), torch.bfloat16, dev)
+        _check(name, t, (B, H, N, d), q.dtype, dev)
     if out is None:
         out = torch.empty_like(q)
-    _check("out", out, (B, H, N, d), torch.bfloat16, dev)
+    _check("out", out, (B, H, N, d), q.dtype, dev)
     if need_lse:
         if lse is None:
             lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         _check("lse", lse, (B, H, N), torch.float32, dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                    lse.data_ptr() if need_lse else None, B, H, N, d, causal,
-                    _scale(scale, d), stream)
+        st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse.data_ptr() if need_lse else None, B, H, N, d, causal,
+                       _scale(scale, d), code, stream)
     if st != FA_OK:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, "fa_fwd_ex")
     return out, lse
 
 
@@ -143,19 +173,20 @@ def backward(do, q, k, v, o, lse, causal: bool = False, scale: float | None = No
     import torch
     B, H, N, d = q.shape
     dev = q.device
+    code = _dtype_code(q)
     for name, t in (("do", do), ("q", q), ("k", k), ("v", v), ("o", o)):
-        _check(name, t, (B, H, N, d), torch.bfloat16, dev)
+        _check(name, t, (B, H, N, d), q.dtype, dev)
     _check("lse", lse, (B, H, N), torch.float32, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check(name, t, (B, H, N, d), torch.bfloat16, dev)
+        _check(name, t, (B, H, N, d), q.dtype, dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                    B, H, N, d, causal, _scale(scale, d), stream)
+        st = fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       B, H, N, d, causal, _scale(scale, d), code, stream)
     if st != FA_OK:
-        raise FAError(st, "fa_bwd")
+        raise FAError(st, "fa_bwd_ex")
     return dq, dk, dv

@@ -42,8 +42,9 @@ int check_tensor(const void* p) {
 
 extern "C" {
 
-int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
-           int d, int causal, float softmax_scale, void* stream) {
+int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+              int N, int d, int causal, float softmax_scale, int dtype, void* stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
   int st = check_common(B, H, N, d, causal, softmax_scale);
   if (st != FA_OK) return st;
   for (const void* p : {Q, K, V, (const void*)O})
@@ -51,13 +52,19 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   if (LSE != nullptr && !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
 
   fa::FwdArgs a{Q, K, V, O, LSE, B, H, N, d, causal != 0, softmax_scale,
-                reinterpret_cast<hipStream_t>(stream)};
+                reinterpret_cast<hipStream_t>(stream), dtype == FA_DTYPE_F16};
   return hip_status(fa::launch_fwd(a), FA_ERR_HIP);
 }
 
-int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
-           const void* dO, void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal,
-           float softmax_scale, void* stream) {
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+           int d, int causal, float softmax_scale, void* stream) {
+  return fa_fwd_ex(Q, K, V, O, LSE, B, H, N, d, causal, softmax_scale, FA_DTYPE_BF16, stream);
+}
+
+int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+              const void* dO, void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal,
+              float softmax_scale, int dtype, void* stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
   int st = check_common(B, H, N, d, causal, softmax_scale);
   if (st != FA_OK) return st;
   for (const void* p : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
@@ -70,10 +77,17 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
   if (m != hipSuccess || scratch == nullptr)
     return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
   fa::BwdArgs a{Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal != 0, softmax_scale, s,
-                static_cast<float*>(scratch)};
+                static_cast<float*>(scratch), dtype == FA_DTYPE_F16};
   const hipError_t e = fa::launch_bwd(a);
   const hipError_t f = hipFreeAsync(scratch, s);
   return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+           const void* dO, void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal,
+           float softmax_scale, void* stream) {
+  return fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal, softmax_scale,
+                   FA_DTYPE_BF16, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -81,7 +95,8 @@ const char* fa_status_string(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_INVALID_ARG:
       return "FA_ERR_INVALID_ARG: null or misaligned pointer, bad shape, scale or causal flag";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128, element type bf16 or f16";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call or kernel launch failed";
     case FA_ERR_OUT_OF_MEMORY: return "FA_ERR_OUT_OF_MEMORY: backward scratch allocation failed";
     default: return "unknown fa_status";

@@ -40,7 +40,7 @@ namespace fa {
 // ---------------------------------------------------------------------------
 // 1. Row statistics
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
                                                      const __bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE,
@@ -55,8 +55,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
     const u32x4 b = ld_global16(dO + row * D + 8 * c);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      acc += __uint_as_float(a[m] << 16) * __uint_as_float(b[m] << 16);
-      acc += __uint_as_float(a[m] & 0xFFFF0000u) * __uint_as_float(b[m] & 0xFFFF0000u);
+      acc += lo16<F16>(a[m]) * lo16<F16>(b[m]);
+      acc += hi16<F16>(a[m]) * hi16<F16>(b[m]);
     }
   }
 #pragma unroll
@@ -94,7 +94,7 @@ struct BwdCfg {
 // so on each SIMD the products of one wave overlap the vector work of the
 // other. Q, dO tiles and row statistics of three steps are resident (s - 1,
 // s, and s + 1 being loaded straight from HBM into LDS).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -218,7 +218,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      sd[i % QB] = mfma32(ar[i % R], frag[i / QB], sd[i % QB]);
+      sd[i % QB] = mfma32x<F16>(ar[i % R], frag[i / QB], sd[i % QB]);
       if (i + R < NP) ar[i % R] = rd(i + R);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -242,7 +242,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int ks = i / NB;
-      acc_kd[i % NB] = mfma32(as_bf16x8(opnd[ks >> 1][ks & 1]), br[i % R], acc_kd[i % NB]);
+      acc_kd[i % NB] = mfma32x<F16>(as_bf16x8(opnd[ks >> 1][ks & 1]), br[i % R], acc_kd[i % NB]);
       if (i + R < NP) br[i % R] = rd(i + R);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -281,8 +281,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           for (int e = 0; e < 4; ++e) p[e] = (unsigned)(m0 + e + mbase) >= mbound ? 0.f : p[e];
         }
         // registers 4g..4g+3 are elements 4(g%2)..+3 of k-step g/2
-        opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
-        opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
+        opnd[qb][g >> 1][2 * (g & 1)] = pack2<F16>(p[0], p[1]);
+        opnd[qb][g >> 1][2 * (g & 1) + 1] = pack2<F16>(p[2], p[3]);
       }
 #pragma unroll
     for (int j = 0; j < 2 * QB; ++j) psb[kblk][j][lane] = opnd[j >> 1][j & 1];
@@ -304,13 +304,12 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int g = 0; g < 4; ++g) {
         const uint32_t w0 = pp[2 * qb + (g >> 1)][2 * (g & 1)];
         const uint32_t w1 = pp[2 * qb + (g >> 1)][2 * (g & 1) + 1];
-        const float p[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
-                            __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
+        const float p[4] = {lo16<F16>(w0), hi16<F16>(w0), lo16<F16>(w1), hi16<F16>(w1)};
         float ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[qb][4 * g + e] - d4[qb][g][e]);
-        opnd[qb][g >> 1][2 * (g & 1)] = pack_bf16(ds[0], ds[1]);
-        opnd[qb][g >> 1][2 * (g & 1) + 1] = pack_bf16(ds[2], ds[3]);
+        opnd[qb][g >> 1][2 * (g & 1)] = pack2<F16>(ds[0], ds[1]);
+        opnd[qb][g >> 1][2 * (g & 1) + 1] = pack2<F16>(ds[2], ds[3]);
       }
   };
 
@@ -378,15 +377,15 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   else
     run(no{});
 
-  // ---- epilogue: dV = dV_acc (P-waves), dK = scale * dK_acc (dS-waves), bf16 --
-  __bf16* out = pwave ? dV : dK;
+  // ---- epilogue: dV = dV_acc (P-waves), dK = scale * dK_acc (dS-waves) --------
+  uint16_t* out = reinterpret_cast<uint16_t*>(pwave ? dV : dK);
   const float osc = pwave ? 1.f : scale;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kk < N) out[head + (size_t)kk * D + 32 * b + l32] = (__bf16)(acc_kd[b][r] * osc);
+      if (kk < N) out[head + (size_t)kk * D + 32 * b + l32] = to16<F16>(acc_kd[b][r] * osc);
     }
 }
 
@@ -420,7 +419,7 @@ struct DqCfg {
   static_assert(BC * CH % 64 == 0, "tile loads");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -550,7 +549,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           for (int u2 = 0; u2 < 2; ++u2)
             d2[u2] = 32 * kb + 8 * ((r + u2) >> 2) + ((r + u2) & 3) > lim ? 0.f : d2[u2];
         }
-        dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16(d2[0], d2[1]);
+        dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack2<F16>(d2[0], d2[1]);
       }
   };
 
@@ -576,7 +575,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int t = i / (D / 32), b = i % (D / 32);
-        acc[b] = mfma32(ar[i % R], as_bf16x8(dsf[t]), acc[b]);
+        acc[b] = mfma32x<F16>(ar[i % R], as_bf16x8(dsf[t]), acc[b]);
         if (i + R < NP) ar[i % R] = tread(i + R);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -606,9 +605,9 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int st = i / (BC / 32), kb = i % (BC / 32);
-        s[kb] = mfma32(kr[i % R], qf[st], s[kb]);
+        s[kb] = mfma32x<F16>(kr[i % R], qf[st], s[kb]);
         if (i + R < NP) kr[i % R] = kread(i + R);
-        dp[kb] = mfma32(vr[i % R], of[st], dp[kb]);
+        dp[kb] = mfma32x<F16>(vr[i % R], of[st], dp[kb]);
         if (i + R < NP) vr[i % R] = vread(i + R);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -696,13 +695,13 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
-      w[0] = pack_bf16(acc[b][4 * g] * scale, acc[b][4 * g + 1] * scale);
-      w[1] = pack_bf16(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
+      w[0] = pack2<F16>(acc[b][4 * g] * scale, acc[b][4 * g + 1] * scale);
+      w[1] = pack2<F16>(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
       st_global8(Drow + 32 * b + 8 * g + 4 * hh, w);
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   using C = BwdCfg<D>;
   using Cq = DqCfg<D>;
@@ -711,7 +710,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const float c_log2 = a.softmax_scale * kLog2e;
   {
     const long long threads = rows * (D / 8);
-    const hipError_t e = launch_kernel(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)),
+    const hipError_t e = launch_kernel(bwd_pre_kernel<D, F16>, dim3((unsigned)((threads + 255) / 256)),
                                        dim3(256), a.stream, (const __bf16*)a.O, (const __bf16*)a.dO,
                                        a.LSE, rowstat, rows);
     if (e != hipSuccess) return e;
@@ -720,7 +719,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     const int nkb = (a.N + C::BCB - 1) / C::BCB;
     const long long total = (long long)nkb * a.B * a.H;
     const hipError_t e = launch_kernel(
-        bwd_dkdv_kernel<D, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+        bwd_dkdv_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
         (const float*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, c_log2,
         a.softmax_scale);
@@ -729,16 +728,21 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   {
     const int nq = (a.N + Cq::BR - 1) / Cq::BR;
     const long long total = (long long)nq * a.B * a.H;
-    return launch_kernel(bwd_dq_kernel<D, CAUSAL>, dim3((unsigned)total),
+    return launch_kernel(bwd_dq_kernel<D, CAUSAL, F16>, dim3((unsigned)total),
                          dim3(Cq::THREADS), a.stream, (const __bf16*)a.Q, (const __bf16*)a.K,
                          (const __bf16*)a.V, (const __bf16*)a.dO, (const float*)rowstat,
                          (__bf16*)a.dQ, a.N, a.B * a.H, c_log2, a.softmax_scale);
   }
 }
 
+template <bool F16>
+static hipError_t launch_bwd_dt(const BwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_bwd_t<128, true, F16>(a) : launch_bwd_t<128, false, F16>(a);
+  return a.causal ? launch_bwd_t<64, true, F16>(a) : launch_bwd_t<64, false, F16>(a);
+}
+
 hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
-  return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
+  return a.f16 ? launch_bwd_dt<true>(a) : launch_bwd_dt<false>(a);
 }
 
 }  // namespace fa

@@ -24,6 +24,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 // One 32x32x16 bf16 matrix-core product with float32 accumulation.
 // Operand layout for a 64-lane wave (lane l, half h = l / 32):
 //   A (32 x 16): lane l holds row l % 32, k = 8h .. 8h+7
@@ -31,6 +34,17 @@ __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(
 //   C (32 x 32): lane l holds column l % 32, rows 8*(r/4) + 4h + r%4, r = 0..15
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same product on 16-bit operands held as raw bits: bf16 (F16 = false)
+// or IEEE binary16 (F16 = true), float32 accumulation either way.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32x(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Lanes l and l ^ 32 exchange values; returns (own, partner) in some order,
@@ -55,6 +69,34 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2 f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// float32 pair -> packed 16-bit pair of the element type, round to nearest
+// even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32); low half = lo.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  if constexpr (F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+// the low / high 16-bit element of a packed pair, widened exactly to float32
+template <bool F16>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(f16x2, w)[0];
+  else return __uint_as_float(w << 16);
+}
+template <bool F16>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(f16x2, w)[1];
+  else return __uint_as_float(w & 0xFFFF0000u);
+}
+// float32 -> one 16-bit element (bits), round to nearest even
+template <bool F16>
+__device__ __forceinline__ uint16_t to16(float v) {
+  if constexpr (F16) return __builtin_bit_cast(uint16_t, (_Float16)v);
+  else return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 // Buffer resource over `bytes` bytes at `base` (raw addressing, no stride):

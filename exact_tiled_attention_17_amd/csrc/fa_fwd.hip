@@ -82,7 +82,7 @@ __device__ __forceinline__ int voff(int r, int col) {  // element offset of (r, 
 // every SIMD one wave's softmax runs while the other wave's products do.
 // Query rows are dealt in 32-row blocks alternating between the groups, so both
 // reach the causal diagonal on the same key tile.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -233,7 +233,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int e = 0; e < 4; ++e) {
           const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][8 * t + 2 * e], c_log2, neg_m));
           const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][8 * t + 2 * e + 1], c_log2, neg_m));
-          const uint32_t pk = pack_bf16(p0, p1);
+          const uint32_t pk = pack2<F16>(p0, p1);
           pf[2 * kb + t][e] = pk;
           lsum += p0 + p1;
         }
@@ -285,12 +285,12 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int i = 0; i < NM; ++i) {
       if constexpr (do_s) {
         const int st = i / (BC / 32), kb = i % (BC / 32);
-        sacc[kb] = mfma32(kr[i % R], qf[st], sacc[kb]);
+        sacc[kb] = mfma32x<F16>(kr[i % R], qf[st], sacc[kb]);
         if (i + R < NM) kr[i % R] = kread(i + R);
       }
       if constexpr (do_pv) {
         const int tk = i / (D / 32), b = i % (D / 32);
-        o[b] = mfma32(vr[i % R], as_bf16x8(pf[tk]), o[b]);
+        o[b] = mfma32x<F16>(vr[i % R], as_bf16x8(pf[tk]), o[b]);
         if (i + R < NM) vr[i % R] = vread(i + R);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -387,27 +387,32 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
-      w[0] = pack_bf16(o[b][4 * g] * inv, o[b][4 * g + 1] * inv);
-      w[1] = pack_bf16(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
+      w[0] = pack2<F16>(o[b][4 * g] * inv, o[b][4 * g + 1] * inv);
+      w[1] = pack2<F16>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
       st_global8(Orow + 32 * b + 8 * g + 4 * hh, w);
     }
   if (LSE != nullptr && hh == 0)
     LSE[(size_t)bh * N + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdCfg<D>;
   const int nq = (a.N + C::BR - 1) / C::BR;
   const long long total = (long long)nq * a.B * a.H;
-  return launch_kernel(fwd_kernel<D, CAUSAL>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+  return launch_kernel(fwd_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
                        a.LSE, a.N, a.B * a.H, a.softmax_scale * kLog2e);
 }
 
+template <bool F16>
+static hipError_t launch_fwd_dt(const FwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_fwd_t<128, true, F16>(a) : launch_fwd_t<128, false, F16>(a);
+  return a.causal ? launch_fwd_t<64, true, F16>(a) : launch_fwd_t<64, false, F16>(a);
+}
+
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
-  return a.causal ? launch_fwd_t<64, true>(a) : launch_fwd_t<64, false>(a);
+  return a.f16 ? launch_fwd_dt<true>(a) : launch_fwd_dt<false>(a);
 }
 
 }  // namespace fa

@@ -16,6 +16,7 @@ struct FwdArgs {
   bool causal;
   float softmax_scale;
   hipStream_t stream;
+  bool f16;  // element type of Q, K, V, O: IEEE binary16 (true) or bf16
 };
 
 struct BwdArgs {
@@ -33,6 +34,7 @@ struct BwdArgs {
   float softmax_scale;
   hipStream_t stream;
   float* rowstat; // 2 x [B,H,N] float32 scratch: LSE in base 2 for every row, then D = dO . O
+  bool f16;       // element type of the 16-bit tensors: IEEE binary16 (true) or bf16
 };
 
 // Enqueues `kernel` and returns the status of this launch alone (not the

@@ -20,18 +20,22 @@
  *   dQ_i = softmax_scale * sum_j dS_ij k_j,   dK_j = softmax_scale * sum_i dS_ij q_i
  *
  * Layout. Every tensor is dense and contiguous in row-major order:
- *   Q, K, V, O, dO, dQ, dK, dV : [B, H, N, d] bfloat16 (raw 16-bit storage)
+ *   Q, K, V, O, dO, dQ, dK, dV : [B, H, N, d] 16-bit floats (raw 16-bit storage):
+ *                                bfloat16 for fa_fwd / fa_bwd, bfloat16 or IEEE
+ *                                binary16 (fa_dtype) for fa_fwd_ex / fa_bwd_ex
  *   LSE                        : [B, H, N]    float32
- * Pointers are device pointers on the current HIP device. bf16 tensors must be
- * 16-byte aligned, LSE 4-byte aligned. Outputs are overwritten, never
+ * Pointers are device pointers on the current HIP device. 16-bit tensors must
+ * be 16-byte aligned, LSE 4-byte aligned. Outputs are overwritten, never
  * accumulated into; they must not alias the inputs.
  *
  * Limits: d in {64, 128}; N >= 1; B, H >= 1; N * d < 2^31 and
  * B * H * ceil(N / 32) < 2^31; softmax_scale finite and > 0; causal in {0, 1}.
  *
- * Precision. Inputs are read as bf16; both contractions run on bf16 matrix
- * cores with float32 accumulation; the softmax runs in float32. O, dQ, dK, dV
- * are rounded to bf16 with round-to-nearest-even; LSE is float32.
+ * Precision. Inputs are read in their element type; both contractions run on
+ * matrix cores of that type (bf16 or f16) with float32 accumulation; the
+ * softmax runs in float32, and P and dS enter the products in the element
+ * type. O, dQ, dK, dV are rounded to the element type with round-to-nearest-
+ * even; LSE is float32.
  *
  * Errors and threading. Every entry point validates its arguments on the host
  * before any HIP call and returns an fa_status. FA_ERR_HIP means a HIP call or
@@ -52,7 +56,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad shape, bad scale or flag */
-  FA_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128 */
+  FA_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128, or unknown fa_dtype */
   FA_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
   FA_ERR_OUT_OF_MEMORY = 4  /* fa_bwd could not get its scratch memory */
 } fa_status;
@@ -93,6 +97,37 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
            int B, int H, int N, int d, int causal, float softmax_scale,
            void* stream);
+
+/*
+ * Element types of the 16-bit tensors. "RTX Flash Attention Implementation
+ * COMPLETE" lists FP16 and BF16 among its Advanced Features (Mixed Precision)
+ * and its Usage Examples build F16 inputs.
+ */
+typedef enum {
+  FA_DTYPE_BF16 = 0, /* bfloat16: 8 exponent bits, 7 mantissa bits */
+  FA_DTYPE_F16 = 1   /* IEEE 754 binary16: 5 exponent bits, 10 mantissa bits */
+} fa_dtype;
+
+/*
+ * fa_fwd with the element type of Q, K, V and O given by `dtype` (an
+ * fa_dtype); fa_fwd is fa_fwd_ex(..., FA_DTYPE_BF16, stream). Same arguments,
+ * layout, ownership and errors as fa_fwd; FA_ERR_UNSUPPORTED for any other
+ * dtype value. For f16 the inputs must be finite binary16 values.
+ */
+int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
+              int B, int H, int N, int d, int causal, float softmax_scale,
+              int dtype, void* stream);
+
+/*
+ * fa_bwd with the element type of Q, K, V, O, dO, dQ, dK and dV given by
+ * `dtype`; fa_bwd is fa_bwd_ex(..., FA_DTYPE_BF16, stream). Same arguments,
+ * scratch, ownership and errors as fa_bwd; FA_ERR_UNSUPPORTED for any other
+ * dtype value.
+ */
+int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
+              const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+              int B, int H, int N, int d, int causal, float softmax_scale,
+              int dtype, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward,
     bf16_bits_to_f64,
+    f16_bits_to_f64,
     causal_visible,
     exact_scale,
     head_backward,

@@ -25,8 +25,10 @@ Readings where the pages are silent (each one is listed in the design notes):
     receives is used exactly (widened to float64).
   * the backward gets the gradient through O only (no gradient w.r.t. LSE).
 
-Every function takes float64 arrays; ``bf16_bits_to_f64`` turns the uint16
-bit patterns the GPU receives into exactly the same values.
+Every function takes float64 arrays; ``bf16_bits_to_f64`` and
+``f16_bits_to_f64`` turn the uint16 bit patterns the GPU receives (bfloat16 or
+IEEE binary16: the Mixed Precision item of the same page's Advanced Features
+names both) into exactly the same values.
 """
 from __future__ import annotations
 
@@ -41,6 +43,15 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u.view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of IEEE binary16 bit patterns (uint16) to float64.
+
+    Every binary16 value (normal, subnormal, zero, infinity) is exactly
+    representable in float64; numpy's float16 type reads the bits as such.
+    """
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
 def exact_scale(scale: float) -> float:

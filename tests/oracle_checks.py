@@ -310,6 +310,21 @@ def check_bf16_decode(orc):
     assert same.all()
 
 
+# --- binary16 decode ---------------------------------------------------------
+def check_f16_decode(orc):
+    import torch
+    rng = _rng(25)
+    bits = np.concatenate([rng.integers(0, 1 << 16, size=4096, dtype=np.uint16),
+                           np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0x7C00, 0xFC00,
+                                     0x3C00, 0xBC00], dtype=np.uint16)])
+    mine = orc.f16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+    # the smallest subnormal and the largest finite value, from their definitions
+    assert mine[-8] == 2.0 ** -24 and mine[-5] == 65504.0 and mine[-4] == np.inf
+
+
 # --- rows_forward agrees with the full forward ---------------------------------
 def check_rows_forward(orc):
     rng = _rng(24)
@@ -336,5 +351,6 @@ ALL_CHECKS = [
     check_torch_cross,
     check_online_recurrence,
     check_bf16_decode,
+    check_f16_decode,
     check_rows_forward,
 ]

@@ -24,7 +24,8 @@ def header_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["fa_bwd", "fa_fwd", "fa_last_hip_error", "fa_status_string"]
+    assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_last_hip_error",
+                                  "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -111,3 +112,23 @@ def test_torch_wrapper_checks_before_calling():
         fa.forward(q, q[:, :, :2], q)
     with pytest.raises(ValueError):
         fa.forward(q[..., ::2], q[..., ::2], q[..., ::2])
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 99])
+def test_ex_entry_points_reject_unknown_dtype(dtype):
+    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == \
+        fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_ex_entry_points_validate_like_the_plain_ones(dtype):
+    # same host-side checks as fa_fwd / fa_bwd for either element type
+    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 16, 96, 0, 0.125, dtype, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 16, 128, 2, 0.125, dtype, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fwd_ex(P + 8, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == \
+        fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_ex(P, P, P, P, None, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == \
+        fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, 0, 2, 16, 128, 0, 0.125, dtype, None) == \
+        fa.FA_ERR_INVALID_ARG

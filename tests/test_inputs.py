@@ -31,6 +31,31 @@ def test_rne_ties_specials_subnormals():
     assert np.array_equal(ai.f32_to_bf16_bits(x), _torch_bf16_bits(x))
 
 
+def _torch_f16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def test_f16_rne_matches_torch():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(200_000) * 10.0 ** rng.uniform(-9, 6, 200_000)).astype(np.float32)
+    # plus ties at binary16 precision, subnormals and overflow
+    extra = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -25, 3 * 2 ** -25, 65520.0, 65519.0,
+                      -70000.0, 0.0, -0.0], np.float32)
+    x = np.concatenate([x, extra])
+    assert np.array_equal(ai.f32_to_f16_bits(x), _torch_f16_bits(x))
+
+
+def test_f16_inputs_same_draws_as_bf16():
+    a = ai.make_qkv(1, 2, 33, 64, 7, sigma_qk=3.0, with_do=True)
+    b = ai.make_qkv(1, 2, 33, 64, 7, sigma_qk=3.0, with_do=True, dtype="f16")
+    for n in ("q", "k", "v", "do"):
+        fa = (a[n].astype(np.uint32) << 16).view(np.float32)
+        fb = b[n].view(np.float16).astype(np.float32)
+        # both are roundings of the same float32 draw: within half an ulp of bf16
+        assert np.all(np.abs(fa - fb) <= np.abs(fb) * 2.0 ** -8 + 1e-30)
+
+
 def test_rne_nan_stays_nan():
     x = np.array([np.nan, -np.nan], np.float32)
     bits = ai.f32_to_bf16_bits(x)

@@ -43,6 +43,8 @@ MUTANTS = {
     "recurrence_alpha_sign": ("alpha = 0.0 if m == -np.inf else np.exp(m - m_new)",
                               "alpha = 0.0 if m == -np.inf else np.exp(m_new - m)"),
     "decode_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "f16_decoded_as_bf16": ("return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)",
+                            "return bf16_bits_to_f64(bits)"),
 }
 
 
