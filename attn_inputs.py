@@ -97,18 +97,22 @@ def normal_f16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
 
 
 def make_qkv(B: int, H: int, N: int, d: int, seed: int, *, sigma_qk: float = 1.0,
-             sigma_v: float = 1.0, with_do: bool = False, dtype: str = "bf16") -> dict:
-    """Q, K, V (and dO) of shape [B, H, N, d] as 16-bit patterns: bf16 by
-    default, IEEE binary16 with dtype="f16" (same draws, other rounding)."""
+             sigma_v: float = 1.0, with_do: bool = False, dtype: str = "bf16",
+             Hkv: int | None = None) -> dict:
+    """Q, K, V (and dO) as 16-bit patterns: bf16 by default, IEEE binary16 with
+    dtype="f16" (same draws, other rounding). Q and dO are [B, H, N, d]; K and
+    V are [B, Hkv, N, d] (Hkv = H unless given)."""
     if dtype not in ("bf16", "f16"):
         raise ValueError(f"dtype must be 'bf16' or 'f16', got {dtype!r}")
+    Hkv = H if Hkv is None else Hkv
     normal = normal_bf16 if dtype == "bf16" else normal_f16
     rng = np.random.default_rng(seed)
     shape = (B, H, N, d)
+    kv_shape = (B, Hkv, N, d)
     out = {
         "q": normal(rng, shape, sigma_qk),
-        "k": normal(rng, shape, sigma_qk),
-        "v": normal(rng, shape, sigma_v),
+        "k": normal(rng, kv_shape, sigma_qk),
+        "v": normal(rng, kv_shape, sigma_v),
     }
     if with_do:
         out["do"] = normal(rng, shape, sigma_v)

@@ -24,6 +24,9 @@ Readings where the pages are silent (each one is listed in the design notes):
   * scale multiplies Q K^T before the softmax; the float32 value the library
     receives is used exactly (widened to float64).
   * the backward gets the gradient through O only (no gradient w.r.t. LSE).
+  * grouped K/V heads (same page, Next Steps & Future Enhancements, Advanced
+    Features: multi-query / grouped-query attention): H / Hkv consecutive
+    query heads share one K/V head; its dK, dV sum over them.
 
 Every function takes float64 arrays; ``bf16_bits_to_f64`` and
 ``f16_bits_to_f64`` turn the uint16 bit patterns the GPU receives (bfloat16 or
@@ -109,27 +112,54 @@ def head_backward(q, k, v, do, causal: bool, scale: float):
     return dq, dk, dv
 
 
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    """The K/V head that query head h attends with, H query heads sharing Hkv.
+
+    "RTX Flash Attention Implementation COMPLETE", Next Steps & Future
+    Enhancements, Advanced Features, names multi-query and grouped-query
+    attention without fixing the grouping. Reading: Hkv divides H, and the
+    query heads form Hkv consecutive groups of H / Hkv, group g sharing K/V
+    head g (Hkv = H: one K/V head per query head; Hkv = 1: one for all).
+    """
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{Hkv} K/V heads cannot serve {H} query heads")
+    return h // (H // Hkv)
+
+
 def attention_forward(q, k, v, causal: bool, scale: float):
-    """O [B,H,N,d] and LSE [B,H,N] (float64) over every (batch, head)."""
+    """O [B,H,N,d] and LSE [B,H,N] (float64) over every (batch, query head).
+
+    q is [B,H,N,d]; k, v are [B,Hkv,N,d], query head h reading K/V head
+    kv_head(h, H, Hkv) (Hkv = H is plain multi-head attention).
+    """
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
     o = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h], v[b, h], causal, scale)
+            g = kv_head(h, H, Hkv)
+            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, g], v[b, g], causal, scale)
     return o, lse
 
 
 def attention_backward(q, k, v, do, causal: bool, scale: float):
-    """dQ, dK, dV [B,H,N,d] (float64) over every (batch, head)."""
-    dq = np.empty_like(q, dtype=np.float64)
-    dk = np.empty_like(k, dtype=np.float64)
-    dv = np.empty_like(v, dtype=np.float64)
+    """dQ [B,H,N,d] and dK, dV [B,Hkv,N,d] (float64).
+
+    A K/V head shared by several query heads enters the loss once per query
+    head, so its gradients are the sums of the per-query-head gradients.
+    """
     B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    dq = np.empty_like(q, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            dq[b, h], dk[b, h], dv[b, h] = head_backward(
-                q[b, h], k[b, h], v[b, h], do[b, h], causal, scale)
+            g = kv_head(h, H, Hkv)
+            dq[b, h], dk_h, dv_h = head_backward(q[b, h], k[b, g], v[b, g], do[b, h], causal, scale)
+            dk[b, g] += dk_h
+            dv[b, g] += dv_h
     return dq, dk, dv
 
 

@@ -337,6 +337,66 @@ def check_rows_forward(orc):
         assert np.allclose(rl, lse[0, 0, rows], rtol=0, atol=1e-13)
 
 
+# --- C16: grouped K/V heads against the scalar brute force ---------------------
+def check_grouped_heads_brute_force(orc):
+    """H query heads over Hkv K/V heads: query head h uses K/V head h Hkv / H
+    (consecutive groups), and a K/V head's gradients are the sums over the
+    query heads of its group of the single-head brute-force gradients."""
+    rng = _rng(26)
+    H, d, scale = 6, 3, 0.8
+    for Hkv in (1, 2, 3, 6):
+        for n in (1, 4, 5):
+            for causal in (False, True):
+                q, do = (_rand(rng, 1, H, n, d, sigma=1.3) for _ in range(2))
+                k, v = (_rand(rng, 1, Hkv, n, d, sigma=1.3) for _ in range(2))
+                o, lse = orc.attention_forward(q, k, v, causal, scale)
+                dq, dk, dv = orc.attention_backward(q, k, v, do, causal, scale)
+                assert dk.shape == k.shape and dv.shape == v.shape
+                ref_dk = np.zeros_like(k)
+                ref_dv = np.zeros_like(v)
+                for h in range(H):
+                    g = h * Hkv // H
+                    bo, blse, bdq, bdk, bdv = brute_force(q[0, h].tolist(), k[0, g].tolist(),
+                                                          v[0, g].tolist(), do[0, h].tolist(),
+                                                          causal, scale)
+                    for mine, ref in ((o[0, h], bo), (lse[0, h], blse), (dq[0, h], bdq)):
+                        ref = np.asarray(ref)
+                        assert np.max(np.abs(mine - ref)) <= 1e-12 * max(1.0, float(np.max(np.abs(ref))))
+                    ref_dk[0, g] += np.asarray(bdk)
+                    ref_dv[0, g] += np.asarray(bdv)
+                for mine, ref in ((dk, ref_dk), (dv, ref_dv)):
+                    assert np.max(np.abs(mine - ref)) <= 1e-12 * max(1.0, float(np.max(np.abs(ref))))
+
+
+# --- C17: grouped K/V heads against torch autograd through repeated K/V -------
+def check_grouped_heads_torch(orc):
+    """Multi-query / grouped-query attention is multi-head attention on K and V
+    with each K/V head repeated for the consecutive query heads of its group;
+    autograd through torch.repeat_interleave sums the repeated gradients."""
+    import torch
+    rng = _rng(27)
+    B, H, n, d = 2, 8, 9, 4
+    for Hkv in (1, 2, 4):
+        for causal in (False, True):
+            q, do = (_rand(rng, B, H, n, d) for _ in range(2))
+            k, v = (_rand(rng, B, Hkv, n, d) for _ in range(2))
+            tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+            kr = tk.repeat_interleave(H // Hkv, dim=1)
+            vr = tv.repeat_interleave(H // Hkv, dim=1)
+            s = torch.matmul(tq, kr.transpose(-1, -2)) * 0.5
+            if causal:
+                s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+            to = torch.matmul(torch.softmax(s, dim=-1), vr)
+            (to * torch.tensor(do)).sum().backward()
+            o, lse = orc.attention_forward(q, k, v, causal, 0.5)
+            dq, dk, dv = orc.attention_backward(q, k, v, do, causal, 0.5)
+            for mine, ref in ((o, to.detach().numpy()),
+                              (lse, torch.logsumexp(s, dim=-1).detach().numpy()),
+                              (dq, tq.grad.numpy()), (dk, tk.grad.numpy()), (dv, tv.grad.numpy())):
+                assert mine.shape == ref.shape
+                assert _max_rel(mine, ref) <= 1e-12, (Hkv, causal)
+
+
 ALL_CHECKS = [
     check_identical_keys,
     check_single_token,
@@ -353,4 +413,6 @@ ALL_CHECKS = [
     check_bf16_decode,
     check_f16_decode,
     check_rows_forward,
+    check_grouped_heads_brute_force,
+    check_grouped_heads_torch,
 ]

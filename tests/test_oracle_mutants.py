@@ -43,6 +43,9 @@ MUTANTS = {
     "recurrence_alpha_sign": ("alpha = 0.0 if m == -np.inf else np.exp(m - m_new)",
                               "alpha = 0.0 if m == -np.inf else np.exp(m_new - m)"),
     "decode_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "gqa_interleaved_groups": ("return h // (H // Hkv)", "return h % Hkv"),
+    "gqa_dk_overwritten": ("dk[b, g] += dk_h", "dk[b, g] = dk_h"),
+    "gqa_dv_overwritten": ("dv[b, g] += dv_h", "dv[b, g] = dv_h"),
     "f16_decoded_as_bf16": ("return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)",
                             "return bf16_bits_to_f64(bits)"),
 }
