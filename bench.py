@@ -114,6 +114,10 @@ def main():
     ap.add_argument("--workload", default="c5", help="attn_inputs workload name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only fa_fwd (profiling aid)")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="K/V heads (grouped-query attention; default: as many as query heads)")
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
+                    help="element type of Q, K, V, O, dO and the gradients")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warmup, run one device-to-device copy of this many MiB "
                          "(a known-size kernel to calibrate HBM byte counters against)")
@@ -131,11 +135,17 @@ def main():
 
     w = ai.WORKLOADS[args.workload]
     causal = True if True in w.causal_modes else False
+    hkv = args.kv_heads or w.H
+    if w.H % hkv:
+        sys.exit(f"--kv-heads {hkv} must divide the {w.H} query heads")
+    # the stored counter figures are for the default launch only
+    default_launch = hkv == w.H and args.dtype == "bf16"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = ai.make_qkv(w.B, w.H, w.N, w.d, w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v,
-                    with_do=True)
-    t = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in x}
+                    with_do=True, dtype=args.dtype, Hkv=hkv)
+    tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    t = {n: torch.from_numpy(x[n].view(np.int16)).view(tdt).to(dev) for n in x}
     del x
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
     o = torch.empty_like(q)
@@ -187,7 +197,8 @@ def main():
         achieved = fl / (tms * 1e-3) / 1e12
         return {"bound": "mfma", "kernel": f"{launch} ({kernels})", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(launch),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(launch) if default_launch else None,
                 "avg_launch_ms": round(tms, 4)}
 
     r_fwd = roof("fa_fwd", "fwd_kernel", f_fwd, t_fwd)
@@ -206,7 +217,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": f"attention fwd+bwd, causal={causal}, B={w.B} H={w.H} N={w.N} "
                                f"d={w.d}, Q,K~N(0,{w.sigma_qk:g}^2), V,dO~N(0,1), seed {w.seed}",
@@ -223,7 +234,12 @@ def main():
         "roofline_fwd": r_fwd,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if hkv != w.H:
+        out["config"]["workload"] += f", {hkv} K/V heads"
+        out["config"]["Hkv"] = hkv
+    if args.dtype != "bf16":
+        out["config"]["workload"] += f", {args.dtype} inputs"
+    if not args.no_cpu_baseline and default_launch:
         out["cpu_baseline"] = cpu_baseline(w, causal)
     print(json.dumps(out), flush=True)
 

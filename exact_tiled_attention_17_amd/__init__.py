@@ -67,9 +67,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fa_fwd.restype = ci
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
     lib.fa_bwd.restype = ci
-    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     lib.fa_fwd_ex.restype = ci
-    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci,
+                              vp]
     lib.fa_bwd_ex.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -99,16 +100,16 @@ def fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal, softmax_scale, s
                          float(softmax_scale), stream or None)
 
 
-def fa_fwd_ex(Q, K, V, O, LSE, B, H, N, d, causal, softmax_scale, dtype, stream) -> int:
-    """C ``fa_fwd_ex``: as ``fa_fwd`` with the element type (FA_DTYPE_*)."""
-    return load().fa_fwd_ex(Q, K, V, O, LSE or None, B, H, N, d, int(causal),
+def fa_fwd_ex(Q, K, V, O, LSE, B, H, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
+    """C ``fa_fwd_ex``: as ``fa_fwd`` with Hkv K/V heads and the element type (FA_DTYPE_*)."""
+    return load().fa_fwd_ex(Q, K, V, O, LSE or None, B, H, Hkv, N, d, int(causal),
                             float(softmax_scale), int(dtype), stream or None)
 
 
-def fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal, softmax_scale, dtype,
+def fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, causal, softmax_scale, dtype,
               stream) -> int:
-    """C ``fa_bwd_ex``: as ``fa_bwd`` with the element type (FA_DTYPE_*)."""
-    return load().fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, int(causal),
+    """C ``fa_bwd_ex``: as ``fa_bwd`` with Hkv K/V heads and the element type (FA_DTYPE_*)."""
+    return load().fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, int(causal),
                             float(softmax_scale), int(dtype), stream or None)
 
 
@@ -135,21 +136,31 @@ def _check(name, t, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _kv_heads(H, k):
+    Hkv = int(k.shape[1])
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"k/v have {Hkv} heads, which must divide the {H} query heads")
+    return Hkv
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, *, out=None, lse=None,
             need_lse: bool = True):
-    """O, LSE = attention(q, k, v). q, k, v: bf16 or float16 [B, H, N, d] on one GPU."""
+    """O, LSE = attention(q, k, v) on one GPU: q bf16 or float16 [B, H, N, d]; k, v of the
+    same dtype, [B, Hkv, N, d] with Hkv dividing H (query head h uses K/V head h // (H // Hkv))."""
     import torch
-    if q.dim() != 4:
-        raise ValueError("q must be [batch, heads, seq_len, head_dim]")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, seq_len, head_dim]")
     B, H, N, d = q.shape
+    Hkv = _kv_heads(H, k)
     dev = q.device
     code = _dtype_code(q)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(name, t, (B, H, N, d), q.dtype, dev)
+    _check("q", q, (B, H, N, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, Hkv, N, d), q.dtype, dev)
     if out is None:
         out = torch.empty_like(q)
     _check("out", out, (B, H, N, d), q.dtype, dev)
@@ -160,7 +171,7 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, out=No
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                       lse.data_ptr() if need_lse else None, B, H, N, d, causal,
+                       lse.data_ptr() if need_lse else None, B, H, Hkv, N, d, causal,
                        _scale(scale, d), code, stream)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_ex")
@@ -169,24 +180,31 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, out=No
 
 def backward(do, q, k, v, o, lse, causal: bool = False, scale: float | None = None, *,
              dq=None, dk=None, dv=None):
-    """dQ, dK, dV of attention given dO, the inputs, and the forward's O and LSE."""
+    """dQ, dK, dV of attention given dO, the inputs, and the forward's O and LSE (shapes as in
+    ``forward``; dK, dV are summed over the query heads that share a K/V head)."""
     import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, seq_len, head_dim]")
     B, H, N, d = q.shape
+    Hkv = _kv_heads(H, k)
     dev = q.device
     code = _dtype_code(q)
-    for name, t in (("do", do), ("q", q), ("k", k), ("v", v), ("o", o)):
+    for name, t in (("do", do), ("q", q), ("o", o)):
         _check(name, t, (B, H, N, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, Hkv, N, d), q.dtype, dev)
     _check("lse", lse, (B, H, N), torch.float32, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check(name, t, (B, H, N, d), q.dtype, dev)
+    _check("dq", dq, (B, H, N, d), q.dtype, dev)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check(name, t, (B, Hkv, N, d), q.dtype, dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                       B, H, N, d, causal, _scale(scale, d), code, stream)
+                       B, H, Hkv, N, d, causal, _scale(scale, d), code, stream)
     if st != FA_OK:
         raise FAError(st, "fa_bwd_ex")
     return dq, dk, dv

@@ -21,8 +21,9 @@ int hip_status(hipError_t e, int status_on_error) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_common(int B, int H, int N, int d, int causal, float scale) {
+int check_common(int B, int H, int Hkv, int N, int d, int causal, float scale) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -43,29 +44,29 @@ int check_tensor(const void* p) {
 extern "C" {
 
 int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
-              int N, int d, int causal, float softmax_scale, int dtype, void* stream) {
+              int Hkv, int N, int d, int causal, float softmax_scale, int dtype, void* stream) {
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
-  int st = check_common(B, H, N, d, causal, softmax_scale);
+  int st = check_common(B, H, Hkv, N, d, causal, softmax_scale);
   if (st != FA_OK) return st;
   for (const void* p : {Q, K, V, (const void*)O})
     if ((st = check_tensor(p)) != FA_OK) return st;
   if (LSE != nullptr && !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
 
   fa::FwdArgs a{Q, K, V, O, LSE, B, H, N, d, causal != 0, softmax_scale,
-                reinterpret_cast<hipStream_t>(stream), dtype == FA_DTYPE_F16};
+                reinterpret_cast<hipStream_t>(stream), dtype == FA_DTYPE_F16, Hkv};
   return hip_status(fa::launch_fwd(a), FA_ERR_HIP);
 }
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
            int d, int causal, float softmax_scale, void* stream) {
-  return fa_fwd_ex(Q, K, V, O, LSE, B, H, N, d, causal, softmax_scale, FA_DTYPE_BF16, stream);
+  return fa_fwd_ex(Q, K, V, O, LSE, B, H, H, N, d, causal, softmax_scale, FA_DTYPE_BF16, stream);
 }
 
 int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
-              const void* dO, void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal,
-              float softmax_scale, int dtype, void* stream) {
+              const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N, int d,
+              int causal, float softmax_scale, int dtype, void* stream) {
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
-  int st = check_common(B, H, N, d, causal, softmax_scale);
+  int st = check_common(B, H, Hkv, N, d, causal, softmax_scale);
   if (st != FA_OK) return st;
   for (const void* p : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
     if ((st = check_tensor(p)) != FA_OK) return st;
@@ -73,11 +74,11 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const 
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* scratch = nullptr;
-  const hipError_t m = hipMallocAsync(&scratch, fa::bwd_scratch_bytes(B, H, N, d), s);
+  const hipError_t m = hipMallocAsync(&scratch, fa::bwd_scratch_bytes(B, H, Hkv, N, d), s);
   if (m != hipSuccess || scratch == nullptr)
     return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
   fa::BwdArgs a{Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal != 0, softmax_scale, s,
-                static_cast<float*>(scratch), dtype == FA_DTYPE_F16};
+                static_cast<float*>(scratch), dtype == FA_DTYPE_F16, Hkv};
   const hipError_t e = fa::launch_bwd(a);
   const hipError_t f = hipFreeAsync(scratch, s);
   return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
@@ -86,7 +87,7 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
            const void* dO, void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal,
            float softmax_scale, void* stream) {
-  return fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal, softmax_scale,
+  return fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, H, N, d, causal, softmax_scale,
                    FA_DTYPE_BF16, stream);
 }
 
@@ -94,7 +95,8 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_INVALID_ARG:
-      return "FA_ERR_INVALID_ARG: null or misaligned pointer, bad shape, scale or causal flag";
+      return "FA_ERR_INVALID_ARG: null or misaligned pointer, bad shape (K/V heads must divide "
+             "query heads), scale or causal flag";
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128, element type bf16 or f16";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call or kernel launch failed";

@@ -94,12 +94,21 @@ struct BwdCfg {
 // so on each SIMD the products of one wave overlap the vector work of the
 // other. Q, dO tiles and row statistics of three steps are resident (s - 1,
 // s, and s + 1 being loaded straight from HBM into LDS).
+// With G query heads per K/V head the workgroup owns a key block of one K/V
+// head and its steps run over the query tiles of each of GS query heads of
+// the group in turn, so dK and dV are summed over them inside the
+// accumulators. When GS < G (few K/V heads: too few workgroups otherwise),
+// the G / GS workgroups of a key block write float32 partial sums to `part`
+// and bwd_reduce_kernel adds them up; with GS == G (part == nullptr) the
+// workgroup writes dK, dV directly.
 template <int D, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ rowstat, __bf16* __restrict__ dK,
-                     __bf16* __restrict__ dV, int N, int BH, float c_log2, float scale) {
+                     __bf16* __restrict__ dV, int N, int BH, int G, int GS, float c_log2,
+                     float scale, float* __restrict__ part) {
+  // BH query heads, BH / G K/V heads; K/V head j serves query heads G j .. G j + G - 1
   using C = BwdCfg<D>;
   constexpr int BCB = C::BCB, BRB = C::BRB, QB = C::QB, CH = C::CH, TI = C::TI;
   // three buffers of each kind, as separate arrays so that every access
@@ -119,8 +128,13 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) float rs2[2 * BRB];
 
   const int nkb = (N + BCB - 1) / BCB;
-  int bh, kb;
-  xcd_remap(blockIdx.x, nkb * BH, nkb, bh, kb);  // causal: low key blocks (most work) first
+  const int BKV = BH / G;  // K/V heads
+  const int S = G / GS;    // workgroups per key block
+  int hs, kb;
+  xcd_remap(blockIdx.x, nkb * BKV * S, nkb, hs, kb);  // causal: low key blocks (most work) first
+  const int bkv = hs / S;
+  const int split = hs - bkv * S;
+  const int qh0 = bkv * G + split * GS;  // first query head this workgroup serves
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -133,15 +147,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tr_e = tr_i >> 2;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
 
-  const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t kvhead = (size_t)bkv * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto rQ = make_rsrc(Q + head, head_bytes);
-  const auto rK = make_rsrc(K + head, head_bytes);
-  const auto rV = make_rsrc(V + head, head_bytes);
-  const auto rdO = make_rsrc(dO + head, head_bytes);
-  // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
-  const auto rL2 = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 4u);
-  const auto rDD = make_rsrc(rowstat + (size_t)BH * N + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rK = make_rsrc(K + kvhead, head_bytes);
+  const auto rV = make_rsrc(V + kvhead, head_bytes);
 
   const int k0 = kb * BCB;
   const int kw0 = k0 + 32 * kblk;  // this wave's first key
@@ -170,8 +179,30 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int m = 0; m < LM; ++m) src_w[m] = src(wave + 8 * m);
   const int nqt = (N + BRB - 1) / BRB;
   const int i0 = CAUSAL ? k0 / BRB : 0;  // first query tile that sees the block's keys
-  auto load_step = [&](int s, __bf16* qd, __bf16* od, float* rsd) __attribute__((always_inline)) {
-    const int q0 = (i0 + s) * BRB;
+  const int nsteps = nqt - i0;           // steps per query head
+  // A step is (g, t): query head qh0 + g, query tile i0 + t. Steps run over
+  // t = 0 .. nsteps - 1 for g = 0 .. GS - 1; the padding steps after the last
+  // keep g = GS - 1 with t >= nsteps, so that all their queries are past N.
+  struct Step {
+    int g, t;
+  };
+  auto advance = [&](Step p) __attribute__((always_inline)) {
+    ++p.t;
+    if (p.t == nsteps && p.g + 1 < GS) {
+      p.t = 0;
+      ++p.g;
+    }
+    return p;
+  };
+  auto load_step = [&](Step p, __bf16* qd, __bf16* od, float* rsd) __attribute__((always_inline)) {
+    const size_t qh = (size_t)(qh0 + p.g);  // query head
+    const size_t head = qh * (size_t)N * D;
+    const auto rQ = make_rsrc(Q + head, head_bytes);
+    const auto rdO = make_rsrc(dO + head, head_bytes);
+    // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
+    const auto rL2 = make_rsrc(rowstat + qh * N, (uint32_t)N * 4u);
+    const auto rDD = make_rsrc(rowstat + (size_t)BH * N + qh * N, (uint32_t)N * 4u);
+    const int q0 = (i0 + p.t) * BRB;
     const uint32_t row0 = (uint32_t)q0 * (D * 2);
 #pragma unroll
     for (int m = 0; m < LM; ++m) {
@@ -257,8 +288,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     mbound = key < N ? (unsigned)(N - qlo) : 0u;
   };
   // P-wave: P = exp2(c S - LSE2) -> opnd (bf16) and to LDS for the partner
-  auto p_phase = [&](int s, const float* rsb, u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
-    const int q0 = (i0 + s) * BRB;
+  auto p_phase = [&](Step p, const float* rsb, u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
+    const int q0 = (i0 + p.t) * BRB;
     const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + BRB > N);
     int mbase;
     unsigned mbound;
@@ -324,25 +355,27 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // second half. The middle slots run in groups of three (buffer index
   // s mod 3, static in each copy); their count is padded to a multiple of 3
   // with steps past the end of the sequence, whose queries are all masked.
-  const int nsteps = nqt - i0;
-  const int last = 3 * ((nsteps + 1) / 3) + 1;  // >= nsteps, == 1 (mod 3)
+  // `cur` is step s, `nxt` step s + 1 (the one being loaded).
+  const int total = GS * nsteps;
+  const int last = 3 * ((total + 1) / 3) + 1;  // >= total, == 1 (mod 3)
   __bf16* const qbuf[3] = {qs0, qs1, qs2};
   __bf16* const obuf[3] = {os0, os1, os2};
   u32x4 (*const pbuf[3])[2 * QB][64] = {ps0, ps1, ps2};
   float* const rbuf[3] = {rs0, rs1, rs2};
   // ROLE: P-wave (true) or dS-wave; each role runs its own straight-line copy
   // of the schedule (same barriers), so neither carries the other's registers
-  auto slot = [&](auto ROLE, auto B3, auto HAS_PREV, auto HAS_CUR, int s) __attribute__((always_inline)) {
+  auto slot = [&](auto ROLE, auto B3, auto HAS_PREV, auto HAS_CUR, int s, Step& cur,
+                  Step& nxt) __attribute__((always_inline)) {
     constexpr bool p_role = decltype(ROLE)::value;
     constexpr int b = decltype(B3)::value, bp = (b + 2) % 3, bn = (b + 1) % 3;
     constexpr bool has_prev = decltype(HAS_PREV)::value, has_cur = decltype(HAS_CUR)::value;
     if constexpr (has_cur)
-      if (s + 1 < last) load_step(s + 1, qbuf[bn], obuf[bn], rbuf[bn]);
+      if (s + 1 < last) load_step(nxt, qbuf[bn], obuf[bn], rbuf[bn]);
     if constexpr (p_role) {
       if constexpr (has_prev) second_product(obuf[bp]);  // dV += P_{s-1}^T dO_{s-1}
       if constexpr (has_cur) {
         first_product(qbuf[b]);                           // S_s
-        p_phase(s, rbuf[b], pbuf[b]);                     // P_s
+        p_phase(cur, rbuf[b], pbuf[b]);                   // P_s
       }
     } else {
       if constexpr (has_prev) {
@@ -353,6 +386,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     wait_vmem_all();  // the loads of step s + 1 have landed
     slot_barrier();
+    cur = nxt;
+    nxt = advance(nxt);
   };
   using c0 = std::integral_constant<int, 0>;
   using c1 = std::integral_constant<int, 1>;
@@ -360,16 +395,18 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   using yes = std::true_type;
   using no = std::false_type;
   auto run = [&](auto ROLE) __attribute__((always_inline)) {
-    slot(ROLE, c0{}, no{}, yes{}, 0);
+    Step cur{0, 0};
+    Step nxt = advance(cur);
+    slot(ROLE, c0{}, no{}, yes{}, 0, cur, nxt);
     for (int s = 1; s < last; s += 3) {
-      slot(ROLE, c1{}, yes{}, yes{}, s);
-      slot(ROLE, c2{}, yes{}, yes{}, s + 1);
-      slot(ROLE, c0{}, yes{}, yes{}, s + 2);
+      slot(ROLE, c1{}, yes{}, yes{}, s, cur, nxt);
+      slot(ROLE, c2{}, yes{}, yes{}, s + 1, cur, nxt);
+      slot(ROLE, c0{}, yes{}, yes{}, s + 2, cur, nxt);
     }
-    slot(ROLE, c1{}, yes{}, no{}, last);
+    slot(ROLE, c1{}, yes{}, no{}, last, cur, nxt);
   };
 
-  load_step(0, qs0, os0, rs0);
+  load_step(Step{0, 0}, qs0, os0, rs0);
   wait_vmem_all();
   __syncthreads();
   if (pwave)
@@ -378,15 +415,48 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     run(no{});
 
   // ---- epilogue: dV = dV_acc (P-waves), dK = scale * dK_acc (dS-waves) --------
-  uint16_t* out = reinterpret_cast<uint16_t*>(pwave ? dV : dK);
   const float osc = pwave ? 1.f : scale;
+  if (part != nullptr) {
+    // float32 partial sums, [dV, dK][split][K/V head][N][D]
+    float* pout = part + ((size_t)(pwave ? 0 : S) + split) * BKV * (size_t)N * D + kvhead;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (kk < N) pout[(size_t)kk * D + 32 * b + l32] = acc_kd[b][r] * osc;
+      }
+    return;
+  }
+  uint16_t* out = reinterpret_cast<uint16_t*>(pwave ? dV : dK);
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kk < N) out[head + (size_t)kk * D + 32 * b + l32] = to16<F16>(acc_kd[b][r] * osc);
+      if (kk < N) out[kvhead + (size_t)kk * D + 32 * b + l32] = to16<F16>(acc_kd[b][r] * osc);
     }
+}
+
+// dV and dK from the float32 partial sums of S workgroups: `part` is
+// [dV, dK][S][n] with n = K/V heads * N * D; each thread sums 4 consecutive
+// elements of one plane and stores them rounded to the 16-bit type.
+template <bool F16>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, int S,
+                                                         long long n, __bf16* __restrict__ dV,
+                                                         __bf16* __restrict__ dK) {
+  const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long quads = n / 4;
+  if (gt >= 2 * quads) return;
+  const int plane = gt >= quads ? 1 : 0;
+  const long long i = 4 * (gt - plane * quads);
+  const float* src = part + (size_t)plane * S * n + i;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(src + (size_t)s * n);
+  u32x2 w;
+  w[0] = pack2<F16>(acc[0], acc[1]);
+  w[1] = pack2<F16>(acc[2], acc[3]);
+  st_global8((plane ? dK : dV) + i, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -424,7 +494,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const float* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
-                   float c_log2, float scale) {
+                   int G, float c_log2, float scale) {
+  // BH query heads; query head bh reads K/V head bh / G
   using C = DqCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, CH = C::CH, TI = C::TI;
   // K tiles in four buffers, V tiles in two; separate arrays so that every
@@ -455,10 +526,11 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
 
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rQ = make_rsrc(Q + head, head_bytes);
-  const auto rK = make_rsrc(K + head, head_bytes);
-  const auto rV = make_rsrc(V + head, head_bytes);
+  const auto rK = make_rsrc(K + kvhead, head_bytes);
+  const auto rV = make_rsrc(V + kvhead, head_bytes);
   const auto rdO = make_rsrc(dO + head, head_bytes);
   // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
   const auto rL2 = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 4u);
@@ -717,13 +789,24 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   }
   {
     const int nkb = (a.N + C::BCB - 1) / C::BCB;
-    const long long total = (long long)nkb * a.B * a.H;
+    const int G = a.H / a.Hkv;
+    const int S = dkdv_splits(a.B, a.H, a.Hkv, a.N, a.d);
+    float* part = S > 1 ? a.rowstat + rowstat_floats(a.B, a.H, a.N) : nullptr;
+    const long long total = (long long)nkb * a.B * a.Hkv * S;
     const hipError_t e = launch_kernel(
         bwd_dkdv_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
-        (const float*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, c_log2,
-        a.softmax_scale);
+        (const float*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, G, G / S,
+        c_log2, a.softmax_scale, part);
     if (e != hipSuccess) return e;
+    if (S > 1) {
+      const long long n = (long long)a.B * a.Hkv * a.N * D;
+      const long long threads = 2 * (n / 4);
+      const hipError_t r = launch_kernel(bwd_reduce_kernel<F16>, dim3((unsigned)((threads + 255) / 256)),
+                                         dim3(256), a.stream, (const float*)part, S, n,
+                                         (__bf16*)a.dV, (__bf16*)a.dK);
+      if (r != hipSuccess) return r;
+    }
   }
   {
     const int nq = (a.N + Cq::BR - 1) / Cq::BR;
@@ -731,7 +814,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     return launch_kernel(bwd_dq_kernel<D, CAUSAL, F16>, dim3((unsigned)total),
                          dim3(Cq::THREADS), a.stream, (const __bf16*)a.Q, (const __bf16*)a.K,
                          (const __bf16*)a.V, (const __bf16*)a.dO, (const float*)rowstat,
-                         (__bf16*)a.dQ, a.N, a.B * a.H, c_log2, a.softmax_scale);
+                         (__bf16*)a.dQ, a.N, a.B * a.H, a.H / a.Hkv, c_log2, a.softmax_scale);
   }
 }
 

@@ -86,7 +86,9 @@ template <int D, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                float* __restrict__ LSE, int N, int BH, float c_log2) {
+                float* __restrict__ LSE, int N, int BH, int G, float c_log2) {
+  // BH query heads; query head bh reads K/V head bh / G (G query heads per
+  // K/V head: 1 for multi-head attention, H for multi-query attention)
   using C = FwdCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, CH = C::CH;
   // Lazy rescaling: the running max used for P only moves when the true row
@@ -122,10 +124,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);
 
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rQ = make_rsrc(Q + head, head_bytes);
-  const auto rK = make_rsrc(K + head, head_bytes);
-  const auto rV = make_rsrc(V + head, head_bytes);
+  const auto rK = make_rsrc(K + kvhead, head_bytes);
+  const auto rV = make_rsrc(V + kvhead, head_bytes);
 
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * rblk;  // first query row of this wave
@@ -402,7 +405,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   const long long total = (long long)nq * a.B * a.H;
   return launch_kernel(fwd_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
-                       a.LSE, a.N, a.B * a.H, a.softmax_scale * kLog2e);
+                       a.LSE, a.N, a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e);
 }
 
 template <bool F16>

@@ -17,6 +17,7 @@ struct FwdArgs {
   float softmax_scale;
   hipStream_t stream;
   bool f16;  // element type of Q, K, V, O: IEEE binary16 (true) or bf16
+  int Hkv;   // K/V heads; divides H (query head h reads K/V head h / (H / Hkv))
 };
 
 struct BwdArgs {
@@ -33,8 +34,10 @@ struct BwdArgs {
   bool causal;
   float softmax_scale;
   hipStream_t stream;
-  float* rowstat; // 2 x [B,H,N] float32 scratch: LSE in base 2 for every row, then D = dO . O
+  float* rowstat; // scratch of bwd_scratch_bytes: 2 x [B,H,N] float32 (LSE in base 2 for
+                  // every row, then D = dO . O), then the dK/dV partial sums if split
   bool f16;       // element type of the 16-bit tensors: IEEE binary16 (true) or bf16
+  int Hkv;        // K/V heads (K, V, dK, dV are [B,Hkv,N,d]); divides H
 };
 
 // Enqueues `kernel` and returns the status of this launch alone (not the
@@ -54,10 +57,37 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 
+// float32 row statistics of the backward: LSE in base 2, then D, per query row
+// (padded to a multiple of 64 floats so that what follows stays 256-byte aligned).
+inline size_t rowstat_floats(int B, int H, int N) {
+  return ((size_t)B * H * N * 2 + 63) / 64 * 64;
+}
+
+// Workgroups that share the query heads of one K/V head in the dK/dV kernel
+// (a divisor S of G = H / Hkv). With few K/V heads, one workgroup per key
+// block would leave most of the 256 compute units idle (multi-query
+// attention: B * ceil(N / 128) workgroups), so the group is split until the
+// grid has 1024 workgroups (four per compute unit), each split writing
+// float32 partial sums (8 * S * B * Hkv * N * d bytes in all, kept under 1 GiB).
+inline int dkdv_splits(int B, int H, int Hkv, int N, int d) {
+  const int G = H / Hkv;
+  const long long blocks = (long long)B * Hkv * ((N + 127) / 128);
+  const long long part_per_split = 8LL * B * Hkv * N * d;
+  int best = 1;
+  for (int S = 2; S <= G; ++S) {
+    if (G % S) continue;
+    if (blocks * best >= 1024 || part_per_split * S > (1LL << 30)) break;
+    best = S;
+  }
+  return best;
+}
+
 // Scratch bytes fa_bwd needs for a problem of this size.
-inline size_t bwd_scratch_bytes(int B, int H, int N, int d) {
-  (void)d;
-  return (size_t)B * H * N * 8;
+inline size_t bwd_scratch_bytes(int B, int H, int Hkv, int N, int d) {
+  const int S = dkdv_splits(B, H, Hkv, N, d);
+  size_t bytes = rowstat_floats(B, H, N) * 4;
+  if (S > 1) bytes += (size_t)S * 8 * B * Hkv * N * d;
+  return bytes;
 }
 
 }  // namespace fa

@@ -18,17 +18,23 @@
  *   dV_j = sum_i P_ij dO_i
  *   dS_ij = P_ij (dO_i . v_j - dO_i . O_i)
  *   dQ_i = softmax_scale * sum_j dS_ij k_j,   dK_j = softmax_scale * sum_i dS_ij q_i
+ * With grouped K/V heads (fa_fwd_ex / fa_bwd_ex, Hkv < H; "RTX Flash
+ * Attention Implementation COMPLETE", Next Steps & Future Enhancements,
+ * Advanced Features: multi-query and grouped-query attention), query head h
+ * attends with K/V head h / (H / Hkv) (integer division), and dK, dV of a K/V
+ * head are the sums of the above over the H / Hkv query heads that share it.
  *
  * Layout. Every tensor is dense and contiguous in row-major order:
  *   Q, K, V, O, dO, dQ, dK, dV : [B, H, N, d] 16-bit floats (raw 16-bit storage):
  *                                bfloat16 for fa_fwd / fa_bwd, bfloat16 or IEEE
  *                                binary16 (fa_dtype) for fa_fwd_ex / fa_bwd_ex
  *   LSE                        : [B, H, N]    float32
+ * except that for fa_fwd_ex / fa_bwd_ex K, V, dK, dV are [B, Hkv, N, d].
  * Pointers are device pointers on the current HIP device. 16-bit tensors must
  * be 16-byte aligned, LSE 4-byte aligned. Outputs are overwritten, never
  * accumulated into; they must not alias the inputs.
  *
- * Limits: d in {64, 128}; N >= 1; B, H >= 1; N * d < 2^31 and
+ * Limits: d in {64, 128}; N >= 1; B, H >= 1; Hkv >= 1 dividing H; N * d < 2^31 and
  * B * H * ceil(N / 32) < 2^31; softmax_scale finite and > 0; causal in {0, 1}.
  *
  * Precision. Inputs are read in their element type; both contractions run on
@@ -88,7 +94,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *   LSE             in : [B,H,N] float32, must not be NULL
  *   dQ, dK, dV      out: [B,H,N,d] bf16
  *
- * Needs float32 scratch of 8*B*H*N bytes, taken stream-ordered with
+ * Needs float32 scratch of 8*B*H*N bytes (rounded up to 256), taken stream-ordered with
  * hipMallocAsync on `stream` and released with hipFreeAsync on the same
  * stream (no host synchronisation). Returns FA_ERR_OUT_OF_MEMORY if it cannot
  * be had.
@@ -109,25 +115,49 @@ typedef enum {
 } fa_dtype;
 
 /*
- * fa_fwd with the element type of Q, K, V and O given by `dtype` (an
- * fa_dtype); fa_fwd is fa_fwd_ex(..., FA_DTYPE_BF16, stream). Same arguments,
- * layout, ownership and errors as fa_fwd; FA_ERR_UNSUPPORTED for any other
- * dtype value. For f16 the inputs must be finite binary16 values.
+ * fa_fwd with Hkv K/V heads and the element type of Q, K, V and O given by
+ * `dtype` (an fa_dtype); fa_fwd(..., H, N, ...) is fa_fwd_ex(..., H, H, N,
+ * ..., FA_DTYPE_BF16, stream).
+ *
+ *   Q        in : [B,H,N,d]     dtype
+ *   K, V     in : [B,Hkv,N,d]   dtype; query head h reads K/V head h / (H / Hkv)
+ *   O        out: [B,H,N,d]     dtype
+ *   LSE      out: [B,H,N] float32, or NULL
+ *
+ * Hkv == H is multi-head attention, Hkv == 1 multi-query attention, anything
+ * between grouped-query attention. Otherwise the same layout, ownership and
+ * errors as fa_fwd: FA_ERR_INVALID_ARG if Hkv < 1 or Hkv does not divide H,
+ * FA_ERR_UNSUPPORTED for an unknown dtype value. For f16 the inputs must be
+ * finite binary16 values.
  */
 int fa_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
-              int B, int H, int N, int d, int causal, float softmax_scale,
-              int dtype, void* stream);
+              int B, int H, int Hkv, int N, int d, int causal,
+              float softmax_scale, int dtype, void* stream);
 
 /*
- * fa_bwd with the element type of Q, K, V, O, dO, dQ, dK and dV given by
- * `dtype`; fa_bwd is fa_bwd_ex(..., FA_DTYPE_BF16, stream). Same arguments,
- * scratch, ownership and errors as fa_bwd; FA_ERR_UNSUPPORTED for any other
- * dtype value.
+ * fa_bwd with Hkv K/V heads and the element type of Q, K, V, O, dO, dQ, dK
+ * and dV given by `dtype`; fa_bwd(..., H, N, ...) is fa_bwd_ex(..., H, H, N,
+ * ..., FA_DTYPE_BF16, stream).
+ *
+ *   Q, O, dO  in : [B,H,N,d]    dtype;  LSE in: [B,H,N] float32, not NULL
+ *   K, V      in : [B,Hkv,N,d]  dtype
+ *   dQ        out: [B,H,N,d]    dtype
+ *   dK, dV    out: [B,Hkv,N,d]  dtype, each summed over the H / Hkv query
+ *                               heads that share the K/V head
+ *
+ * Scratch as in fa_bwd (stream-ordered hipMallocAsync / hipFreeAsync), of
+ * 8*B*H*N bytes (rounded up to 256) plus, when B * Hkv * ceil(N / 128) is
+ * under 1024, 8*S*B*Hkv*N*d bytes of float32 partial sums of dK and dV, where
+ * S > 1 is the smallest divisor of H / Hkv that brings S * B * Hkv *
+ * ceil(N / 128) to 1024, or the largest one whose partial sums stay within
+ * 1 GiB. Same ownership and errors
+ * as fa_bwd, plus FA_ERR_INVALID_ARG if Hkv < 1 or Hkv does not divide H and
+ * FA_ERR_UNSUPPORTED for an unknown dtype value.
  */
 int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
               const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
-              int B, int H, int N, int d, int causal, float softmax_scale,
-              int dtype, void* stream);
+              int B, int H, int Hkv, int N, int d, int causal,
+              float softmax_scale, int dtype, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_string(int status);

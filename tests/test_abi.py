@@ -116,19 +116,42 @@ def test_torch_wrapper_checks_before_calling():
 
 @pytest.mark.parametrize("dtype", [-1, 2, 99])
 def test_ex_entry_points_reject_unknown_dtype(dtype):
-    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == fa.FA_ERR_UNSUPPORTED
-    assert fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == \
+    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 2, 16, 128, 0, 0.125, dtype, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, 1, 2, 2, 16, 128, 0, 0.125, dtype, None) == \
         fa.FA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
 def test_ex_entry_points_validate_like_the_plain_ones(dtype):
     # same host-side checks as fa_fwd / fa_bwd for either element type
-    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 16, 96, 0, 0.125, dtype, None) == fa.FA_ERR_UNSUPPORTED
-    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 16, 128, 2, 0.125, dtype, None) == fa.FA_ERR_INVALID_ARG
-    assert fa.fa_fwd_ex(P + 8, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == \
+    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 2, 16, 96, 0, 0.125, dtype, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_ex(P, P, P, P, P, 1, 2, 2, 16, 128, 2, 0.125, dtype, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fwd_ex(P + 8, P, P, P, P, 1, 2, 2, 16, 128, 0, 0.125, dtype, None) == \
         fa.FA_ERR_INVALID_ARG
-    assert fa.fa_bwd_ex(P, P, P, P, None, P, P, P, P, 1, 2, 16, 128, 0, 0.125, dtype, None) == \
+    assert fa.fa_bwd_ex(P, P, P, P, None, P, P, P, P, 1, 2, 2, 16, 128, 0, 0.125, dtype, None) == \
         fa.FA_ERR_INVALID_ARG
-    assert fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, 0, 2, 16, 128, 0, 0.125, dtype, None) == \
+    assert fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, 0, 2, 2, 16, 128, 0, 0.125, dtype, None) == \
         fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("H,Hkv", [(4, 0), (4, -1), (4, 3), (6, 4), (2, 4)])
+def test_ex_entry_points_reject_kv_heads_not_dividing_query_heads(dtype, H, Hkv):
+    assert fa.fa_fwd_ex(P, P, P, P, P, 1, H, Hkv, 16, 128, 0, 0.125, dtype, None) == \
+        fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, 1, H, Hkv, 16, 128, 0, 0.125, dtype, None) == \
+        fa.FA_ERR_INVALID_ARG
+
+
+def test_torch_wrapper_checks_kv_heads():
+    import torch
+    q = torch.zeros(1, 6, 4, 64, dtype=torch.bfloat16)
+    kv4 = torch.zeros(1, 4, 4, 64, dtype=torch.bfloat16)
+    kv2 = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    kv3 = torch.zeros(1, 3, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):   # 4 does not divide 6
+        fa.forward(q, kv4, kv4)
+    with pytest.raises(ValueError):   # k and v head counts differ
+        fa.forward(q, kv2, kv3)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, kv4, kv4, q, torch.zeros(1, 6, 4))
