@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     head_backward,
     head_forward,
     head_probs,
+    key_mass,
     kv_head,
     online_softmax_stats,
     rows_forward,

@@ -163,6 +163,28 @@ def attention_backward(q, k, v, do, causal: bool, scale: float):
     return dq, dk, dv
 
 
+def key_mass(q, k, causal: bool, scale: float):
+    """Attention mass per key position: mass[b, j] = sum_h sum_i P[b, h, i, j].
+
+    "GPU Performance Optimization Batch 1 - Design Spec", Item 4 (SnapKV +
+    Prefix Caching), Design: during prefill the attention kernel sums the
+    attention weights each key position receives, and a reduction over the
+    heads turns them into one score per key, the importance used to evict
+    keys. Reading: the sum runs over every query row and every query head (a
+    key shared by grouped query heads collects the mass of all of them), P
+    being the forward's exact, masked softmax. q: [B,H,N,d], k: [B,Hkv,N,d];
+    returns [B,N] float64.
+    """
+    B, H, N, _ = q.shape
+    Hkv = k.shape[1]
+    mass = np.zeros((B, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            p, _ = head_probs(q[b, h], k[b, kv_head(h, H, Hkv)], causal, scale)
+            mass[b] += p.sum(axis=0)
+    return mass
+
+
 def rows_forward(q_rows, k, v, rows, causal: bool, scale: float):
     """O and LSE for selected query rows of one head.
 

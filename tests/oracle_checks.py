@@ -397,6 +397,75 @@ def check_grouped_heads_torch(orc):
                 assert _max_rel(mine, ref) <= 1e-12, (Hkv, causal)
 
 
+# --- C18: per-key attention mass: closed forms and invariants ----------------
+def check_key_mass_closed_forms(orc):
+    """Every query row of P sums to 1, so the masses of a batch sum to H N.
+    With all keys equal, P is uniform over the visible keys: each key gets
+    mass H (non-causal), or H sum_{i >= j} 1 / (i + 1) (causal). The last key
+    is seen only by the last query when causal."""
+    rng = _rng(28)
+    for causal in (False, True):
+        for n in (1, 2, 7, 33):
+            B, H, Hkv, d = 2, 4, 2, 5
+            q = _rand(rng, B, H, n, d)
+            k = _rand(rng, B, Hkv, n, d)
+            mass = orc.key_mass(q, k, causal, 0.7)
+            assert mass.shape == (B, n)
+            assert np.allclose(mass.sum(axis=1), H * n, rtol=1e-12, atol=0)
+            assert (mass >= 0).all()
+            if causal:
+                # only query n-1 sees key n-1
+                _, lse = orc.attention_forward(q, k, np.eye(n)[None, None].repeat(B, 0).repeat(Hkv, 1),
+                                               causal, 0.7)
+                sc = float(np.float32(0.7))
+                last = np.zeros(B)
+                for b in range(B):
+                    for h in range(H):
+                        g = h * Hkv // H
+                        last[b] += math.exp(sc * float(q[b, h, n - 1] @ k[b, g, n - 1]) - lse[b, h, n - 1])
+                assert np.allclose(mass[:, n - 1], last, rtol=1e-12, atol=0)
+            kc = np.repeat(_rand(rng, B, Hkv, 1, d), n, axis=2)  # identical keys
+            mass = orc.key_mass(q, kc, causal, 0.7)
+            if causal:
+                ref = np.array([H * math.fsum(1.0 / (i + 1) for i in range(j, n)) for j in range(n)])
+            else:
+                ref = np.full(n, float(H))
+            assert np.allclose(mass, ref[None, :], rtol=1e-12, atol=0)
+
+
+# --- C19: per-key attention mass against torch softmax and a scalar brute force -
+def check_key_mass_cross(orc):
+    import torch
+    rng = _rng(29)
+    for causal in (False, True):
+        B, H, Hkv, n, d = 2, 6, 3, 11, 4
+        q = _rand(rng, B, H, n, d, sigma=1.5)
+        k = _rand(rng, B, Hkv, n, d, sigma=1.5)
+        tq = torch.tensor(q)
+        tk = torch.tensor(k).repeat_interleave(H // Hkv, dim=1)
+        s = torch.matmul(tq, tk.transpose(-1, -2)) * float(np.float32(0.45))
+        if causal:
+            s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+        ref = torch.softmax(s, dim=-1).sum(dim=(1, 2)).numpy()
+        assert _max_rel(orc.key_mass(q, k, causal, 0.45), ref) <= 1e-12
+    # scalar brute force (one batch, one head per K/V head)
+    for causal in (False, True):
+        q = _rand(rng, 1, 2, 5, 3)
+        k = _rand(rng, 1, 2, 5, 3)
+        mass = orc.key_mass(q, k, causal, 0.9)
+        ref = [0.0] * 5
+        sc = float(np.float32(0.9))
+        for h in range(2):
+            for i in range(5):
+                keys = range(i + 1) if causal else range(5)
+                s = {j: sc * math.fsum(q[0, h, i, c] * k[0, h, j, c] for c in range(3)) for j in keys}
+                m = max(s.values())
+                tot = math.fsum(math.exp(v - m) for v in s.values())
+                for j in keys:
+                    ref[j] += math.exp(s[j] - m) / tot
+        assert np.max(np.abs(mass[0] - np.asarray(ref))) <= 1e-12 * max(ref)
+
+
 ALL_CHECKS = [
     check_identical_keys,
     check_single_token,
@@ -415,4 +484,6 @@ ALL_CHECKS = [
     check_rows_forward,
     check_grouped_heads_brute_force,
     check_grouped_heads_torch,
+    check_key_mass_closed_forms,
+    check_key_mass_cross,
 ]

@@ -46,6 +46,10 @@ MUTANTS = {
     "gqa_interleaved_groups": ("return h // (H // Hkv)", "return h % Hkv"),
     "gqa_dk_overwritten": ("dk[b, g] += dk_h", "dk[b, g] = dk_h"),
     "gqa_dv_overwritten": ("dv[b, g] += dv_h", "dv[b, g] = dv_h"),
+    "mass_row_sums": ("mass[b] += p.sum(axis=0)", "mass[b] += p.sum(axis=1)"),
+    "mass_last_head_only": ("mass[b] += p.sum(axis=0)", "mass[b] = p.sum(axis=0)"),
+    "mass_kv_head_by_query_head": ("p, _ = head_probs(q[b, h], k[b, kv_head(h, H, Hkv)], causal, scale)",
+                                   "p, _ = head_probs(q[b, h], k[b, h % Hkv], causal, scale)"),
     "f16_decoded_as_bf16": ("return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)",
                             "return bf16_bits_to_f64(bits)"),
 }
