@@ -182,6 +182,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the per-key attention mass (a second pass after the forward, not part of
+    # the training step): timed on its own, same stream, same inputs
+    mass_ms = None
+    if not args.fwd_only:
+        mass = torch.empty((w.B, w.N), dtype=torch.float32, device=dev)
+        fa.key_mass(q, k, lse, causal, w.scale, out=mass)
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in mev:
+            e0.record(stream)
+            fa.key_mass(q, k, lse, causal, w.scale, out=mass)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        mass_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if not args.fwd_only else [0.0]
     f_fwd, f_bwd = flops(w, causal)
@@ -205,6 +220,9 @@ def main():
     r_bwd = roof("fa_bwd", "bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel", f_bwd, t_bwd) \
         if not args.fwd_only else None
     roofline = r_bwd if (r_bwd is not None and t_bwd >= t_fwd) else r_fwd
+    # S = Q K^T is the pass's only product: half the forward's FLOPs
+    r_mass = roof("fa_key_mass", "key_mass_kernel + key_mass_reduce_kernel", f_fwd / 2, mass_ms) \
+        if mass_ms is not None else None
 
     out = {
         "metric": "bf16 attention TFLOP/s fwd & fwd+bwd at 4x64x4096x128 causal, % MFMA peak",
@@ -232,6 +250,7 @@ def main():
         "page_context_ms": PAGE_TIMES_MS.get(w.label),
         "roofline": roofline,
         "roofline_fwd": r_fwd,
+        "roofline_key_mass": r_mass,
         "cpu_baseline": None,
     }
     if hkv != w.H:

@@ -1,9 +1,10 @@
 """Exact tiled attention for AMD Instinct MI355X (gfx950).
 
 A thin binding of ``libfa.so`` (C ABI in ``include/fa.h``). The functions
-``fa_fwd``, ``fa_bwd``, ``fa_fwd_ex``, ``fa_bwd_ex`` and ``fa_status_string``
-mirror the C entry points one to one (raw device pointers as Python ints, ``stream`` as a hipStream_t
-handle). ``forward`` and ``backward`` are conveniences over torch tensors:
+``fa_fwd``, ``fa_bwd``, ``fa_fwd_ex``, ``fa_bwd_ex``, ``fa_key_mass`` and
+``fa_status_string`` mirror the C entry points one to one (raw device
+pointers as Python ints, ``stream`` as a hipStream_t handle). ``forward``,
+``backward`` and ``key_mass`` are conveniences over torch tensors:
 they check dtypes and shapes, allocate outputs with torch and pass
 ``data_ptr()`` and the current stream; every step of the computation runs in
 the library's HIP kernels. There is no fallback: if the library is missing
@@ -19,8 +20,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_status_string", "fa_last_hip_error",
-           "forward", "backward", "load", "FAError", "LIB_PATH", "FA_DTYPE_BF16", "FA_DTYPE_F16"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_key_mass", "fa_status_string",
+           "fa_last_hip_error",
+           "forward", "backward", "key_mass", "load", "FAError", "LIB_PATH", "FA_DTYPE_BF16", "FA_DTYPE_F16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -72,6 +74,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci,
                               vp]
     lib.fa_bwd_ex.restype = ci
+    lib.fa_key_mass.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.fa_key_mass.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -111,6 +115,12 @@ def fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, causal, softmax_
     """C ``fa_bwd_ex``: as ``fa_bwd`` with Hkv K/V heads and the element type (FA_DTYPE_*)."""
     return load().fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, int(causal),
                             float(softmax_scale), int(dtype), stream or None)
+
+
+def fa_key_mass(Q, K, LSE, mass, B, H, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
+    """C ``fa_key_mass``: per-key attention mass summed over heads; returns the status."""
+    return load().fa_key_mass(Q, K, LSE, mass, B, H, Hkv, N, d, int(causal), float(softmax_scale),
+                              int(dtype), stream or None)
 
 
 def _dtype_code(t):
@@ -208,3 +218,28 @@ def backward(do, q, k, v, o, lse, causal: bool = False, scale: float | None = No
     if st != FA_OK:
         raise FAError(st, "fa_bwd_ex")
     return dq, dk, dv
+
+
+def key_mass(q, k, lse, causal: bool = False, scale: float | None = None, *, out=None):
+    """mass[b, j] = sum over heads and query rows of the attention probability key j gets
+    (float32 [B, N]), from q, k (as in ``forward``) and the forward's LSE."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k must be [batch, heads, seq_len, head_dim]")
+    B, H, N, d = q.shape
+    Hkv = _kv_heads(H, k)
+    dev = q.device
+    code = _dtype_code(q)
+    _check("q", q, (B, H, N, d), q.dtype, dev)
+    _check("k", k, (B, Hkv, N, d), q.dtype, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=dev)
+    _check("out", out, (B, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = fa_key_mass(q.data_ptr(), k.data_ptr(), lse.data_ptr(), out.data_ptr(), B, H, Hkv, N, d,
+                         causal, _scale(scale, d), code, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_key_mass")
+    return out

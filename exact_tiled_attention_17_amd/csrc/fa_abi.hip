@@ -91,6 +91,28 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
                    FA_DTYPE_BF16, stream);
 }
 
+int fa_key_mass(const void* Q, const void* K, const float* LSE, float* mass, int B, int H, int Hkv,
+                int N, int d, int causal, float softmax_scale, int dtype, void* stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
+  int st = check_common(B, H, Hkv, N, d, causal, softmax_scale);
+  if (st != FA_OK) return st;
+  for (const void* p : {Q, K})
+    if ((st = check_tensor(p)) != FA_OK) return st;
+  if (LSE == nullptr || !aligned(LSE, 4) || mass == nullptr || !aligned(mass, 4))
+    return FA_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* part = nullptr;
+  const hipError_t m = hipMallocAsync(&part, (size_t)B * H * N * 4, s);
+  if (m != hipSuccess || part == nullptr)
+    return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
+  fa::MassArgs a{Q, K, LSE, mass, static_cast<float*>(part), B, H, Hkv, N, d, causal != 0,
+                 softmax_scale, s, dtype == FA_DTYPE_F16};
+  const hipError_t e = fa::launch_mass(a);
+  const hipError_t f = hipFreeAsync(part, s);
+  return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
@@ -100,7 +122,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128, element type bf16 or f16";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call or kernel launch failed";
-    case FA_ERR_OUT_OF_MEMORY: return "FA_ERR_OUT_OF_MEMORY: backward scratch allocation failed";
+    case FA_ERR_OUT_OF_MEMORY: return "FA_ERR_OUT_OF_MEMORY: scratch allocation failed";
     default: return "unknown fa_status";
   }
 }

@@ -131,10 +131,6 @@ __device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ f32x4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
-// float32 atomic add through a buffer resource; out-of-range offsets are dropped.
-__device__ __forceinline__ void buf_atomic_add(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
-}
 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -166,30 +162,6 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Interleave four rows of eight bf16 (one 16-byte chunk each, rows r0..r3)
-// into eight 4-element columns: column e = (r0[e], r1[e], r2[e], r3[e]).
-// Used to write a transposed tile into LDS with 8-byte stores.
-__device__ __forceinline__ void transpose4x8(const u32x4& r0, const u32x4& r1, const u32x4& r2,
-                                             const u32x4& r3, u32x2 col[8]) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint32_t a = r0[m], b = r1[m], c = r2[m], d = r3[m];
-    // even element (low halves) and odd element (high halves) of dword m
-    col[2 * m][0] = (a & 0xFFFFu) | (b << 16);
-    col[2 * m][1] = (c & 0xFFFFu) | (d << 16);
-    col[2 * m + 1][0] = (a >> 16) | (b & 0xFFFF0000u);
-    col[2 * m + 1][1] = (c >> 16) | (d & 0xFFFF0000u);
-  }
-}
-
-// Position of item x (0..15 within each group of 16) in a transposed operand
-// tile: bits 2 and 3 swap. With the MFMA C layout above, a lane's 8 values for
-// one 16-wide k step are items {4h..4h+3, 8+4h..8+4h+3}; after this swap they
-// sit at positions 8h..8h+7, so a B/A-operand read is one 16-byte load.
-__device__ __forceinline__ int kperm(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
 // Row-major tiles of d-wide rows keep 16-byte chunk c of row r at chunk
 // position c ^ swz(r). For d = 128 the swizzle makes both access patterns
 // conflict-free: 16 consecutive rows at one chunk (operand rows), and 4
@@ -206,7 +178,7 @@ __device__ __forceinline__ int tile_off(int r, int col) {  // element offset of 
 // Maps a linear workgroup id to (head, tile) so that the workgroups that land
 // on one XCD (the hardware deals ids round-robin over the 8 XCDs) cover whole
 // heads, which then share that XCD's L2; within an XCD, heads go one after the
-// other and each head's tiles go in the order `tile_of` gives.
+// other, each head's tiles in increasing order.
 __device__ __forceinline__ void xcd_remap(int bid, int total, int tiles, int& head, int& tile) {
   int v = bid;
   if (total % kXcds == 0) {

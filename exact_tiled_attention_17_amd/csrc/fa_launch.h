@@ -40,6 +40,19 @@ struct BwdArgs {
   int Hkv;        // K/V heads (K, V, dK, dV are [B,Hkv,N,d]); divides H
 };
 
+struct MassArgs {
+  const void* Q;
+  const void* K;
+  const float* LSE;
+  float* mass;   // [B, N] float32 output
+  float* part;   // [B*H, N] float32 scratch: per-head column sums
+  int B, H, Hkv, N, d;
+  bool causal;
+  float softmax_scale;
+  hipStream_t stream;
+  bool f16;
+};
+
 // Enqueues `kernel` and returns the status of this launch alone (not the
 // runtime's sticky last error, which other libraries in the process may have
 // left behind).
@@ -56,6 +69,7 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_mass(const MassArgs& a);
 
 // float32 row statistics of the backward: LSE in base 2, then D, per query row
 // (padded to a multiple of 64 floats so that what follows stays 256-byte aligned).

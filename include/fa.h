@@ -64,7 +64,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad shape, bad scale or flag */
   FA_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128, or unknown fa_dtype */
   FA_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
-  FA_ERR_OUT_OF_MEMORY = 4  /* fa_bwd could not get its scratch memory */
+  FA_ERR_OUT_OF_MEMORY = 4  /* fa_bwd or fa_key_mass could not get its scratch memory */
 } fa_status;
 
 /*
@@ -158,6 +158,33 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
               const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
               int B, int H, int Hkv, int N, int d, int causal,
               float softmax_scale, int dtype, void* stream);
+
+/*
+ * Attention mass per key position ("GPU Performance Optimization Batch 1 -
+ * Design Spec", Item 4, SnapKV + Prefix Caching, Design: the attention weights
+ * each key position receives during prefill are summed and reduced over the
+ * heads, giving the importance score that decides which keys to evict):
+ *
+ *   mass[b, j] = sum over query heads h and query rows i of P[b, h, i, j]
+ *
+ * with P the softmax probabilities of fa_fwd_ex (same causal flag, scale and
+ * K/V grouping), recomputed from Q, K and the forward's LSE.
+ *
+ *   Q     in : [B,H,N,d]    dtype
+ *   K     in : [B,Hkv,N,d]  dtype; query head h reads K head h / (H / Hkv)
+ *   LSE   in : [B,H,N] float32 as written by fa_fwd_ex for these Q, K; not NULL
+ *   mass  out: [B,N] float32, 4-byte aligned, overwritten
+ *
+ * Every query row's probabilities sum to 1, so each batch's masses sum to
+ * H * N. P is computed in float32 from the float32 S of the matrix cores and
+ * summed in float32, per head in a fixed order, then over the heads in order
+ * 0 .. H-1: the result is deterministic. Needs B*H*N*4 bytes of scratch,
+ * taken and released stream-ordered on `stream` like fa_bwd's. Limits and
+ * errors as fa_fwd_ex; FA_ERR_OUT_OF_MEMORY if the scratch cannot be had.
+ */
+int fa_key_mass(const void* Q, const void* K, const float* LSE, float* mass,
+                int B, int H, int Hkv, int N, int d, int causal,
+                float softmax_scale, int dtype, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -24,8 +24,8 @@ def header_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_last_hip_error",
-                                  "fa_status_string"]
+    assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_key_mass",
+                                  "fa_last_hip_error", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -155,3 +155,35 @@ def test_torch_wrapper_checks_kv_heads():
         fa.forward(q, kv2, kv3)
     with pytest.raises(ValueError):
         fa.backward(q, q, kv4, kv4, q, torch.zeros(1, 6, 4))
+
+
+def mass(**kw):
+    a = dict(GOOD, Q=P, K=P, LSE=P, mass=P, Hkv=2, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_key_mass(a["Q"], a["K"], a["LSE"], a["mass"], a["B"], a["H"], a["Hkv"], a["N"],
+                          a["d"], a["causal"], a["softmax_scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "LSE", "mass"])
+def test_key_mass_rejects_null_and_misaligned(name):
+    assert mass(**{name: None}) == fa.FA_ERR_INVALID_ARG
+    assert mass(**{name: P + 2}) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), "FA_ERR_UNSUPPORTED"), (dict(dtype=5), "FA_ERR_UNSUPPORTED"),
+    (dict(N=0), "FA_ERR_INVALID_ARG"), (dict(B=0), "FA_ERR_INVALID_ARG"),
+    (dict(Hkv=3), "FA_ERR_INVALID_ARG"), (dict(causal=2), "FA_ERR_INVALID_ARG"),
+    (dict(softmax_scale=0.0), "FA_ERR_INVALID_ARG"), (dict(softmax_scale=float("nan")), "FA_ERR_INVALID_ARG"),
+])
+def test_key_mass_validates(kw, status):
+    assert mass(**kw) == getattr(fa, status)
+
+
+def test_torch_key_mass_checks_before_calling():
+    import torch
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):   # lse of the wrong shape
+        fa.key_mass(q, q, torch.zeros(1, 2, 5))
+    with pytest.raises(TypeError):    # lse not float32
+        fa.key_mass(q, q, torch.zeros(1, 2, 4, dtype=torch.float64))
