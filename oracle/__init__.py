@@ -19,3 +19,11 @@ from .attention import (  # noqa: F401
     online_softmax_stats,
     rows_forward,
 )
+from .fp8 import (  # noqa: F401
+    block_exponent,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_round,
+    fp8_attention_forward,
+    quantize_e4m3_blocks,
+)

@@ -466,6 +466,138 @@ def check_key_mass_cross(orc):
         assert np.max(np.abs(mass[0] - np.asarray(ref))) <= 1e-12 * max(ref)
 
 
+# --- C20: E4M3 decode and rounding against torch's float8_e4m3fn ------------
+def check_e4m3_against_torch(orc):
+    """All 256 codes decode as torch's float8_e4m3fn; rounding float32 values
+    in [-448, 448] (every grid point, every midpoint between neighbours, and
+    random draws at several magnitudes) gives torch's value and byte, zero
+    taken as +0."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert ((mine == ref) | (np.isnan(mine) & np.isnan(ref))).all()
+    grid = np.unique(mine[np.isfinite(mine)])
+    rng = _rng(30)
+    ys = np.concatenate([grid, (grid[1:] + grid[:-1]) / 2, rng.uniform(-448, 448, 20000),
+                         rng.standard_normal(20000) * 0.02, rng.standard_normal(2000) * 2.0 ** -8])
+    ys = ys.astype(np.float32).astype(np.float64)
+    r = orc.e4m3_round(ys)
+    t = torch.from_numpy(ys.astype(np.float32)).to(torch.float8_e4m3fn)
+    tv = t.to(torch.float64).numpy()
+    assert np.array_equal(r, np.where(tv == 0, 0.0, tv))
+    tb = t.view(torch.uint8).numpy().copy()
+    tb[(tb & 0x7F) == 0] = 0
+    assert np.array_equal(orc.e4m3_encode(r), tb)
+    assert np.array_equal(orc.e4m3_decode(orc.e4m3_encode(r)), r)
+
+
+# --- C21: block scale exponents: closed forms ---------------------------------
+def check_block_exponent(orc):
+    """amax = 448 * 2^k needs exactly e = k; anything above it k + 1; half of
+    it k - 1; 0 gives 0; tiny blocks stop at -100. On random blocks the
+    largest scaled magnitude lands in (224, 448]."""
+    for k in (-20, -3, 0, 1, 7, 30):
+        a = 448.0 * 2.0 ** k
+        assert orc.block_exponent(np.array([a]))[0] == k
+        assert orc.block_exponent(np.array([np.nextafter(a, np.inf)]))[0] == k + 1
+        assert orc.block_exponent(np.array([a / 2]))[0] == k - 1
+        assert orc.block_exponent(np.array([np.nextafter(a / 2, np.inf)]))[0] == k
+    assert orc.block_exponent(np.array([0.0]))[0] == 0
+    assert orc.block_exponent(np.array([2.0 ** -120]))[0] == -100
+    rng = _rng(31)
+    x = rng.standard_normal((3, 37, 64)) * np.exp(rng.uniform(-5, 5, (3, 1, 1)))
+    _, expo, _ = orc.quantize_e4m3_blocks(x)
+    for r in range(3):
+        for rb in range(expo.shape[1]):
+            for cb in range(expo.shape[2]):
+                blk = x[r, 16 * rb:16 * rb + 16, 16 * cb:16 * cb + 16]
+                top = np.abs(blk).max() / 2.0 ** expo[r, rb, cb]
+                assert 224.0 < top <= 448.0
+
+
+# --- C22: block quantisation: locality, error bound, fixed points -------------
+def check_block_quantisation(orc):
+    """Each 16 x 16 block is quantised on its own (changing one element moves
+    only its block), the error of a value is at most half an E4M3 step at the
+    block's scale, values already on a block's grid are kept exactly, and the
+    ragged last row block of a head holds only its own rows."""
+    rng = _rng(32)
+    R, N, d = 2, 45, 64
+    x = rng.standard_normal((R, N, d))
+    codes, expo, deq = orc.quantize_e4m3_blocks(x)
+    assert codes.shape == (R, N, d) and expo.shape == (R, 3, 4)
+    # error bound at the block's scale: |y - y~| <= step / 2 with y = x / 2^e,
+    # y~ = x~ / 2^e and step = 2^(max(floor(log2 |y|), -6) - 3)
+    scl = 2.0 ** np.repeat(np.repeat(expo, 16, axis=1)[:, :N], 16, axis=2)
+    y, yq = x / scl, deq / scl
+    _, ex = np.frexp(np.abs(y))
+    step = 2.0 ** (np.maximum(ex - 1, -6) - 3)
+    assert np.all(np.abs(y - yq) <= step / 2)
+    # locality
+    x2 = x.copy()
+    x2[1, 20, 40] *= 100.0
+    c2, e2, _ = orc.quantize_e4m3_blocks(x2)
+    changed = np.argwhere(c2 != codes)
+    assert len(changed) > 0
+    assert set(map(tuple, changed[:, :1])) == {(1,)}
+    assert all(16 <= r < 32 and 32 <= c < 48 for _, r, c in changed)
+    assert np.argwhere(e2 != expo).tolist() == [[1, 1, 2]]
+    # fixed points: E4M3 values times 2^e with a 448 in each block
+    grid = orc.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    z = rng.choice(np.concatenate([grid, -grid]), size=(1, 32, 32)) * 2.0 ** -5
+    z[0, ::16, ::16] = 448.0 * 2.0 ** -5
+    zc, ze, zd = orc.quantize_e4m3_blocks(z)
+    assert np.array_equal(zd, z) and (ze == -5).all()
+    assert np.array_equal(orc.e4m3_decode(zc) * 2.0 ** -5, z)
+    # idempotent: the dequantised values are their own quantisation
+    assert np.array_equal(orc.quantize_e4m3_blocks(deq)[2], deq)
+    # the ragged last block: rows 32..44 only
+    x3 = x.copy()
+    x3[:, 44] = 0.0
+    _, e3, d3 = orc.quantize_e4m3_blocks(x3[:, :44])
+    assert np.array_equal(d3, orc.quantize_e4m3_blocks(x3)[2][:, :44])
+
+
+# --- C23: the FP8 forward is exact attention on the dequantised operands -------
+def check_fp8_forward(orc):
+    """Inputs already on their blocks' grids pass through unchanged, so the
+    FP8 forward equals the plain forward there; on general inputs it differs
+    from the plain forward by no more than the quantisation of Q and K can
+    explain (a first-order bound from |dS| <= |dQ||K| + |Q||dK|)."""
+    rng = _rng(33)
+    grid = orc.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    for causal in (False, True):
+        q = rng.choice(np.concatenate([grid, -grid]), size=(1, 2, 20, 32)) * 2.0 ** -7
+        k = rng.choice(np.concatenate([grid, -grid]), size=(1, 1, 20, 32)) * 2.0 ** -7
+        q[..., ::16, ::16] = 448.0 * 2.0 ** -7
+        k[..., ::16, ::16] = 448.0 * 2.0 ** -7
+        v = rng.standard_normal((1, 1, 20, 32))
+        o8, l8 = orc.fp8_attention_forward(q, k, v, causal, 0.3)
+        o, lse = orc.attention_forward(q, k, v, causal, 0.3)
+        assert np.array_equal(o8, o) and np.array_equal(l8, lse)
+        q = rng.standard_normal((2, 4, 33, 32))
+        k = rng.standard_normal((2, 2, 33, 32))
+        v = rng.standard_normal((2, 2, 33, 32))
+        o8, l8 = orc.fp8_attention_forward(q, k, v, causal, 0.3)
+        o, lse = orc.attention_forward(q, k, v, causal, 0.3)
+        qd = orc.quantize_e4m3_blocks(q.reshape(8, 33, 32))[2].reshape(q.shape)
+        kd = orc.quantize_e4m3_blocks(k.reshape(4, 33, 32))[2].reshape(k.shape)
+        kr = np.repeat(k, 2, axis=1)
+        dkr = np.repeat(np.abs(kd - k), 2, axis=1)
+        ds = 0.3 * (np.abs(qd - q) @ np.abs(kr).swapaxes(-1, -2) + np.abs(q) @ dkr.swapaxes(-1, -2))
+        bound = ds.max()
+        assert 0 < np.abs(l8 - lse).max() <= bound
+        assert np.abs(o8 - o).max() <= 2 * bound * np.abs(v).max()
+        # quantising is idempotent, so feeding the dequantised Q and K gives
+        # the same result: both operands are quantised, and only once
+        o8b, l8b = orc.fp8_attention_forward(qd, kd, v, causal, 0.3)
+        assert np.array_equal(o8b, o8) and np.array_equal(l8b, l8)
+        o8c, _ = orc.fp8_attention_forward(qd, k, v, causal, 0.3)
+        o8d, _ = orc.fp8_attention_forward(q, kd, v, causal, 0.3)
+        assert np.array_equal(o8c, o8) and np.array_equal(o8d, o8)
+
+
 ALL_CHECKS = [
     check_identical_keys,
     check_single_token,
@@ -486,4 +618,8 @@ ALL_CHECKS = [
     check_grouped_heads_torch,
     check_key_mass_closed_forms,
     check_key_mass_cross,
+    check_e4m3_against_torch,
+    check_block_exponent,
+    check_block_quantisation,
+    check_fp8_forward,
 ]

@@ -5,7 +5,6 @@ term, a wrong sign, a wrong index or axis, a transposed operand), the copy is
 loaded as a separate module on the CPU, and the full pin battery must reject it.
 The real oracle is never modified.
 """
-import importlib.util
 import os
 import types
 
@@ -13,8 +12,8 @@ import pytest
 
 from tests import oracle_checks as oc
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "oracle", "attention.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "attention.py")
 
 MUTANTS = {
     "dropped_scale": ("s = sc * (q @ k.T)", "s = (q @ k.T)"),
@@ -50,18 +49,39 @@ MUTANTS = {
     "mass_last_head_only": ("mass[b] += p.sum(axis=0)", "mass[b] = p.sum(axis=0)"),
     "mass_kv_head_by_query_head": ("p, _ = head_probs(q[b, h], k[b, kv_head(h, H, Hkv)], causal, scale)",
                                    "p, _ = head_probs(q[b, h], k[b, h % Hkv], causal, scale)"),
+    # FP8 path (oracle/fp8.py)
+    "e4m3_round_half_up": ("fp8", "r = np.round(a / step) * step", "r = np.floor(a / step + 0.5) * step"),
+    "e4m3_subnormal_step": ("fp8", "expo = np.maximum(ex - 1, -6)          # binade",
+                            "expo = np.maximum(ex - 1, -7)          # binade"),
+    "e4m3_encode_mantissa": ("fp8", "np.where(normal, 8.0, 1.0)", "np.where(normal, 16.0, 1.0)"),
+    "block_exponent_strict": ("fp8", "e = np.where(m <= 0.875, ex - 9, ex - 8)",
+                              "e = np.where(m < 0.875, ex - 9, ex - 8)"),
+    "block_exponent_floor": ("fp8", "e = np.where(m <= 0.875, ex - 9, ex - 8)", "e = ex - 9"),
+    "block_amax_whole_rows": ("fp8", "e = block_exponent(np.abs(blk).max(axis=(1, 2)))",
+                              "e = block_exponent(np.abs(x[:, rows, :]).max(axis=(1, 2)))"),
+    "dequant_without_scale": ("fp8", "deq[:, rows, cols] = np.ldexp(v, e[:, None, None])",
+                              "deq[:, rows, cols] = v"),
+    "fp8_forward_unquantised_k": ("fp8", "return attention_forward(qd.reshape(q.shape), kd.reshape(k.shape), v, causal, scale)",
+                                  "return attention_forward(qd.reshape(q.shape), k, v, causal, scale)"),
     "f16_decoded_as_bf16": ("return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)",
                             "return bf16_bits_to_f64(bits)"),
 }
 
 
-def _load_mutant(name, old, new):
-    with open(SRC) as f:
+def _load_mutant(name, *spec):
+    """The oracle with one edit planted: a namespace holding every oracle
+    function, those of the edited module taken from the edited copy."""
+    import oracle
+    fname, old, new = spec if len(spec) == 3 else ("attention", *spec)
+    with open(os.path.join(ORACLE_DIR, fname + ".py")) as f:
         text = f.read()
-    assert text.count(old) == 1, f"mutation {name} does not match the oracle source exactly once"
-    mod = types.ModuleType(f"oracle_mutant_{name}")
+    assert text.count(old) == 1, f"mutation {name} does not match oracle/{fname}.py exactly once"
+    mod = types.ModuleType(f"oracle.mutant_{name}")
+    mod.__package__ = "oracle"  # relative imports resolve to the real package
     exec(compile(text.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
-    return mod
+    ns = {k: getattr(oracle, k) for k in dir(oracle) if not k.startswith("_")}
+    ns.update({k: v for k, v in mod.__dict__.items() if not k.startswith("_")})
+    return types.SimpleNamespace(**ns)
 
 
 def _battery_fails(mod):
@@ -75,14 +95,12 @@ def _battery_fails(mod):
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
-    old, new = MUTANTS[name]
-    mod = _load_mutant(name, old, new)
+    mod = _load_mutant(name, *MUTANTS[name])
     caught_by = _battery_fails(mod)
     assert caught_by is not None, f"planted mistake {name!r} passed every pin"
 
 
-def test_unmutated_copy_passes():
-    spec = importlib.util.spec_from_file_location("oracle_copy", SRC)
-    mod = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mod)
-    assert _battery_fails(mod) is None
+@pytest.mark.parametrize("fname,anchor", [("attention", "def key_mass("), ("fp8", "def e4m3_round(")])
+def test_unmutated_copy_passes(fname, anchor):
+    # the same loading path with an edit that changes nothing
+    assert _battery_fails(_load_mutant("identity", fname, anchor, anchor)) is None
