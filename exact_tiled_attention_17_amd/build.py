@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_mass.hip", "fa_abi.hip"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_mass.hip", "fa_fp8.hip", "fa_abi.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

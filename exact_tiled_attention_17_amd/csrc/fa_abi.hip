@@ -113,6 +113,48 @@ int fa_key_mass(const void* Q, const void* K, const float* LSE, float* mass, int
   return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
 }
 
+int fa_quantize_e4m3(const void* X, void* codes, float* scales, int R, int N, int d, int dtype,
+                     void* stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
+  if (R < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)N * d >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  if ((long long)R * ((N + 15) / 16) >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  int st = check_tensor(X);
+  if (st != FA_OK) return st;
+  if (codes == nullptr || !aligned(codes, 16) || scales == nullptr || !aligned(scales, 4))
+    return FA_ERR_INVALID_ARG;
+  fa::QuantArgs a{X, static_cast<uint8_t*>(codes), scales, nullptr, R, N, d,
+                  reinterpret_cast<hipStream_t>(stream), dtype == FA_DTYPE_F16};
+  return hip_status(fa::launch_quant(a), FA_ERR_HIP);
+}
+
+int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+               int Hkv, int N, int d, int causal, float softmax_scale, void* stream) {
+  int st = check_common(B, H, Hkv, N, d, causal, softmax_scale);
+  if (st != FA_OK) return st;
+  for (const void* p : {Q, K, V, (const void*)O})
+    if ((st = check_tensor(p)) != FA_OK) return st;
+  if (LSE != nullptr && !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t q_bytes = (size_t)B * H * N * d * 2, k_bytes = (size_t)B * Hkv * N * d * 2;
+  void* scratch = nullptr;  // dequantised Q, then K (bf16)
+  const hipError_t m = hipMallocAsync(&scratch, q_bytes + k_bytes, s);
+  if (m != hipSuccess || scratch == nullptr)
+    return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
+  char* qd = static_cast<char*>(scratch);
+  char* kd = qd + q_bytes;
+  hipError_t e = fa::launch_quant(fa::QuantArgs{Q, nullptr, nullptr, qd, B * H, N, d, s, false});
+  if (e == hipSuccess)
+    e = fa::launch_quant(fa::QuantArgs{K, nullptr, nullptr, kd, B * Hkv, N, d, s, false});
+  if (e == hipSuccess)
+    e = fa::launch_fwd(fa::FwdArgs{qd, kd, V, O, LSE, B, H, N, d, causal != 0, softmax_scale, s,
+                                   false, Hkv});
+  const hipError_t f = hipFreeAsync(scratch, s);
+  return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

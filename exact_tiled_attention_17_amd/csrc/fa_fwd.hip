@@ -11,10 +11,10 @@
 //  * Both products are computed transposed, S^T = K Q^T and O^T = V^T P^T,
 //    on 32x32x16 bf16 matrix cores. In the accumulator layout of S^T every lane
 //    then holds 16 scores of a single query row (its partner lane l ^ 32 holds
-//    the other 16), so the row max needs one cross-lane swap, the row sum none
-//    until the end, and the rescale factor of a lane's O^T accumulators is the
-//    lane's own. P^T goes from the S^T registers straight into the B operand of
-//    the second product (no LDS round trip); the V^T operand comes from the
+//    the other 16), so the row max needs one cross-lane swap and the rescale
+//    factor of a lane's O^T accumulators is the lane's own. P^T goes from the
+//    S^T registers straight into the B operand of the second product (no LDS
+//    round trip); the V^T operand comes from the
 //    row-major V tile through gfx950's transposing LDS read, rows taken in the
 //    key order of the P^T operand.
 //  * K/V tiles of BC = 64 keys are staged in LDS, double buffered, and loaded
@@ -29,8 +29,13 @@
 //    the work of tiles fully masked for its own rows; masks are applied only to
 //    tiles that cross the diagonal or the end of the sequence.
 //  * The softmax runs in base 2 in float32: c = scale * log2(e) is folded into
-//    one FMA per score; P is rounded to bf16 for the matrix core, the row sum l
-//    is accumulated in float32 from the unrounded values. The reference max
+//    one FMA per score; P is rounded to bf16 for the matrix core. The row sum
+//    l is a product too: an all-ones A operand against the same P^T operands
+//    sums the rounded P per query, so l adds exactly the weights the P V
+//    product uses (O is a convex combination of V rows up to float32 sums; with
+//    the unrounded P in l, a row dominated by one key would carry that key's
+//    rounding error, up to 2^-8 |V|, into O) and costs the vector ALUs
+//    nothing. The reference max
 //    only moves when the row max outgrows it by 2^8, so the O^T rescale runs on
 //    few tiles.
 //  * Global reads go through buffer resources: rows past the end of the
@@ -196,7 +201,9 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   f32x16 sacc[BC / 32];     // S^T of the tile being processed
   u32x4 pf[BC / 16];        // P^T of the previous tile, bf16, as B operands
   float m_run = -INFINITY;  // reference max of c * s for this row (base-2 units)
-  float l_run = 0.f;        // this lane's share of the running sum
+  // running sum of the row's rounded P, from the matrix cores: every element
+  // holds it (the A operand is all ones); only element 0 is rescaled and read
+  f32x16 lacc = f32x16{};
 
   // online softmax of sacc (key tile u) -> pf; rescales o, l
   auto softmax = [&](int u) __attribute__((always_inline)) {
@@ -222,12 +229,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
       m_run = m_new;
-      l_run *= alpha;
+      lacc[0] *= alpha;
 #pragma unroll
       for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
     }
     const float neg_m = -m_run;
-    float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -238,9 +244,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][8 * t + 2 * e + 1], c_log2, neg_m));
           const uint32_t pk = pack2<F16>(p0, p1);
           pf[2 * kb + t][e] = pk;
-          lsum += p0 + p1;
+
         }
-    l_run += lsum;
   };
 
   // Per-lane element offsets of the transposing V^T reads, one per d block:
@@ -254,8 +259,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     asm volatile("" : "+v"(vrow[b]));
   }
 
-  // M phase: S_u = K_u Q^T into sacc (if DO_S) and O^T += V_t P_t^T (if DO_PV),
-  // the two product streams interleaved. Operands stream through register rings
+  // M phase: S_u = K_u Q^T into sacc (if DO_S) and O^T += V_t P_t^T with
+  // l += 1 P_t^T (if DO_PV), the product streams interleaved. Operands stream through register rings
   // two products deep (fenced so the scheduler keeps that depth instead of
   // hoisting every read, which would not fit the register budget).
   auto mphase = [&](auto DO_S, auto DO_PV, const __bf16* kt, const __bf16* vt) __attribute__((always_inline)) {
@@ -272,6 +277,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     };
     constexpr int R = RING;
     bf16x8 kr[R], vr[R];
+    const uint32_t one2 = F16 ? 0x3C003C00u : 0x3F803F80u;
+    const bf16x8 ones = as_bf16x8(u32x4{one2, one2, one2, one2});
     if constexpr (do_s) {
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) sacc[kb] = f32x16{};
@@ -295,6 +302,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const int tk = i / (D / 32), b = i % (D / 32);
         o[b] = mfma32x<F16>(vr[i % R], as_bf16x8(pf[tk]), o[b]);
         if (i + R < NM) vr[i % R] = vread(i + R);
+        // l += sum over this key step of the rounded P, per query
+        if (b == D / 32 - 1) lacc = mfma32x<F16>(ones, as_bf16x8(pf[tk]), lacc);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -381,7 +390,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l) ------------------------
   if (!wave_active) return;
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = lacc[0];
   if (row >= N) return;
   const float inv = 1.f / l_tot;
   __bf16* Orow = O + head + (size_t)row * D;

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -53,6 +54,16 @@ struct MassArgs {
   bool f16;
 };
 
+struct QuantArgs {
+  const void* X;    // [R, N, d] 16-bit input
+  uint8_t* codes;   // [R, N, d] E4M3 codes, or nullptr
+  float* scales;    // [R, ceil(N / 16), d / 16] block scales (powers of two), or nullptr
+  void* deq;        // [R, N, d] bf16 dequantised values, or nullptr
+  int R, N, d;
+  hipStream_t stream;
+  bool f16;
+};
+
 // Enqueues `kernel` and returns the status of this launch alone (not the
 // runtime's sticky last error, which other libraries in the process may have
 // left behind).
@@ -70,6 +81,7 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_mass(const MassArgs& a);
+hipError_t launch_quant(const QuantArgs& a);
 
 // float32 row statistics of the backward: LSE in base 2, then D, per query row
 // (padded to a multiple of 64 floats so that what follows stays 256-byte aligned).

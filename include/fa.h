@@ -40,8 +40,12 @@
  * Precision. Inputs are read in their element type; both contractions run on
  * matrix cores of that type (bf16 or f16) with float32 accumulation; the
  * softmax runs in float32, and P and dS enter the products in the element
- * type. O, dQ, dK, dV are rounded to the element type with round-to-nearest-
- * even; LSE is float32.
+ * type. The row sum that normalises O adds P as rounded to the element type,
+ * the weights the P V product uses, so O is a convex combination of V rows up
+ * to float32 sums; LSE is taken from the same sum, which puts it within
+ * ln(1 + 2^-8) (bf16; ln(1 + 2^-11) for f16) of the exact log-sum-exp. O, dQ,
+ * dK, dV are rounded to the element type with round-to-nearest-even; LSE is
+ * float32.
  *
  * Errors and threading. Every entry point validates its arguments on the host
  * before any HIP call and returns an fa_status. FA_ERR_HIP means a HIP call or
@@ -64,7 +68,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad shape, bad scale or flag */
   FA_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128, or unknown fa_dtype */
   FA_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
-  FA_ERR_OUT_OF_MEMORY = 4  /* fa_bwd or fa_key_mass could not get its scratch memory */
+  FA_ERR_OUT_OF_MEMORY = 4  /* fa_bwd, fa_key_mass or fa_fwd_fp8 could not get its scratch */
 } fa_status;
 
 /*
@@ -176,7 +180,8 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
  *   mass  out: [B,N] float32, 4-byte aligned, overwritten
  *
  * Every query row's probabilities sum to 1, so each batch's masses sum to
- * H * N. P is computed in float32 from the float32 S of the matrix cores and
+ * H * N (within a factor 1 +- 2^-8 with the LSE of fa_fwd_ex on bf16, whose
+ * row sums add the rounded P). P is computed in float32 from the float32 S of the matrix cores and
  * summed in float32, per head in a fixed order, then over the heads in order
  * 0 .. H-1: the result is deterministic. Needs B*H*N*4 bytes of scratch,
  * taken and released stream-ordered on `stream` like fa_bwd's. Limits and
@@ -185,6 +190,45 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
 int fa_key_mass(const void* Q, const void* K, const float* LSE, float* mass,
                 int B, int H, int Hkv, int N, int d, int causal,
                 float softmax_scale, int dtype, void* stream);
+
+/*
+ * FP8 (E4M3) quantisation of 16 x 16 blocks ("GPU Performance Optimization
+ * Batch 1 - Design Spec", Item 3, Design, optional FP8 path: each 16 x 16
+ * block of Q and K is quantised to E4M3 with a per-block scale factor; Item 2,
+ * Design, Step 1: the E4M3 cast saturates at +-448).
+ *
+ *   X       in : [R, N, d] 16-bit (dtype), R matrices (heads) of N rows
+ *   codes   out: [R, N, d] uint8 E4M3 codes (OCP E4M3: sign, 4 exponent bits
+ *                with bias 7, 3 mantissa bits), 16-byte aligned
+ *   scales  out: [R, ceil(N/16), d/16] float32, one per block, 4-byte aligned
+ *
+ * A block is 16 consecutive rows (fewer in the last row block) x 16
+ * consecutive columns of one matrix. Its scale is 2^e for the smallest integer
+ * e with amax <= 448 * 2^e (amax: the block's largest magnitude), but at
+ * least 2^-100, and 1 for an all-zero block. codes = the E4M3 value nearest to
+ * x / 2^e (ties to even; zero encoded as 0x00), so x ~ decode(code) * scale
+ * and no value saturates. Inputs must be finite. Allocates nothing. Errors:
+ * FA_ERR_INVALID_ARG (null or misaligned pointer, R or N < 1, N*d >= 2^31),
+ * FA_ERR_UNSUPPORTED (d not 64 or 128, unknown dtype).
+ */
+int fa_quantize_e4m3(const void* X, void* codes, float* scales, int R, int N,
+                     int d, int dtype, void* stream);
+
+/*
+ * Forward pass of the FP8 path (same page, Item 3, Design, optional FP8
+ * path): Q and K are quantised per 16 x 16 block as fa_quantize_e4m3 does,
+ * and O, LSE are exact attention on the dequantised decode(code) * scale
+ * values of Q and K, with V, P and O as in fa_fwd_ex. Arguments, layout and
+ * errors as fa_fwd_ex with dtype bf16 (the only element type of this path;
+ * there is no FP8 backward). The dequantised values have at most 4
+ * significant bits, so the bf16 matrix products use them exactly. Inputs must
+ * be finite with magnitudes below 2^120. Takes 2*(B*H + B*Hkv)*N*d bytes of
+ * scratch (the dequantised Q and K), stream-ordered like fa_bwd's;
+ * FA_ERR_OUT_OF_MEMORY if it cannot be had.
+ */
+int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int B, int H, int Hkv, int N, int d, int causal,
+               float softmax_scale, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -24,8 +24,9 @@ def header_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_key_mass",
-                                  "fa_last_hip_error", "fa_status_string"]
+    assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_fwd_fp8",
+                                  "fa_key_mass", "fa_last_hip_error", "fa_quantize_e4m3",
+                                  "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -187,3 +188,49 @@ def test_torch_key_mass_checks_before_calling():
         fa.key_mass(q, q, torch.zeros(1, 2, 5))
     with pytest.raises(TypeError):    # lse not float32
         fa.key_mass(q, q, torch.zeros(1, 2, 4, dtype=torch.float64))
+
+
+def quant(**kw):
+    a = dict(X=P, codes=P, scales=P, R=2, N=16, d=128, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_quantize_e4m3(a["X"], a["codes"], a["scales"], a["R"], a["N"], a["d"], a["dtype"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), "FA_ERR_INVALID_ARG"), (dict(X=P + 2), "FA_ERR_INVALID_ARG"),
+    (dict(codes=None), "FA_ERR_INVALID_ARG"), (dict(codes=P + 4), "FA_ERR_INVALID_ARG"),
+    (dict(scales=None), "FA_ERR_INVALID_ARG"), (dict(scales=P + 2), "FA_ERR_INVALID_ARG"),
+    (dict(R=0), "FA_ERR_INVALID_ARG"), (dict(N=0), "FA_ERR_INVALID_ARG"),
+    (dict(N=1 << 24, d=128), "FA_ERR_INVALID_ARG"),
+    (dict(d=96), "FA_ERR_UNSUPPORTED"), (dict(dtype=3), "FA_ERR_UNSUPPORTED"),
+])
+def test_quantize_validates(kw, status):
+    assert quant(**kw) == getattr(fa, status)
+
+
+def fwd8(**kw):
+    a = dict(GOOD, Q=P, K=P, V=P, O=P, LSE=P, Hkv=2, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["Hkv"], a["N"],
+                         a["d"], a["causal"], a["softmax_scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), "FA_ERR_INVALID_ARG"), (dict(K=P + 2), "FA_ERR_INVALID_ARG"),
+    (dict(V=None), "FA_ERR_INVALID_ARG"), (dict(O=P + 8), "FA_ERR_INVALID_ARG"),
+    (dict(LSE=P + 2), "FA_ERR_INVALID_ARG"), (dict(Hkv=3), "FA_ERR_INVALID_ARG"),
+    (dict(N=0), "FA_ERR_INVALID_ARG"), (dict(causal=5), "FA_ERR_INVALID_ARG"),
+    (dict(softmax_scale=-1.0), "FA_ERR_INVALID_ARG"), (dict(d=32), "FA_ERR_UNSUPPORTED"),
+])
+def test_fwd_fp8_validates(kw, status):
+    assert fwd8(**kw) == getattr(fa, status)
+
+
+def test_torch_fp8_wrappers_check_before_calling():
+    import torch
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.float16)
+    with pytest.raises(TypeError):    # the FP8 forward takes bf16 only
+        fa.forward_fp8(q, q, q)
+    with pytest.raises(TypeError):
+        fa.quantize_e4m3(q.float())

@@ -9,8 +9,11 @@ Tolerance. The kernel recomputes S exactly up to float32 accumulation, takes
 P = exp2(c S - LSE2) with the forward's float32 LSE, and sums in float32, so a
 mass carries the relative error of its P entries: |dS| c + |dLSE| plus float32
 summation over up to H N terms, about 1e-5 in practice. The bar is
-max |mass_gpu - mass_ref| <= 1e-3 max |mass_ref|, with the oracle's own LSE
-fed in (the kernel alone) and with the GPU forward's LSE (the pipeline).
+max |mass_gpu - mass_ref| <= 1e-3 max |mass_ref| with the oracle's own LSE fed
+in (the kernel alone). With the GPU forward's LSE (the pipeline) the bar is
+2^-8: that LSE normalises by the sum of the bf16-rounded P (the weights of the
+forward's P V product), so a row's recomputed probabilities sum to 1 within a
+factor 1 +- 2^-8.
 """
 import math
 
@@ -24,6 +27,7 @@ from tests.gpu_util import announce, max_abs, rel_to_max, to_dev, to_f64
 pytestmark = pytest.mark.gpu
 
 MASS_RTOL = 1e-3
+PIPE_RTOL = 2.0 ** -8
 
 
 def _dec(x):
@@ -51,11 +55,12 @@ def test_mass_small_every_key(fa, H, Hkv, N, causal, d):
     _, lse = fa.forward(q, k, v, causal, scale)
     m2 = fa.key_mass(q, k, lse, causal, scale)
     torch.cuda.synchronize()
-    for m in (m1, m2):
+    for m, tol in ((m1, MASS_RTOL), (m2, PIPE_RTOL)):
         assert tuple(m.shape) == (B, N)
-        assert rel_to_max(to_f64(m), ref) <= MASS_RTOL
+        assert rel_to_max(to_f64(m), ref) <= tol
     # each query row's probabilities sum to 1
-    assert np.allclose(to_f64(m2).sum(1), H * N, rtol=1e-4)
+    assert np.allclose(to_f64(m1).sum(1), H * N, rtol=1e-4)
+    assert np.allclose(to_f64(m2).sum(1), H * N, rtol=PIPE_RTOL)
 
 
 def test_mass_identical_keys_closed_form(fa):
@@ -76,7 +81,7 @@ def test_mass_identical_keys_closed_form(fa):
             ref = H * tail
         else:
             ref = np.full(N, float(H))
-        assert rel_to_max(m, np.broadcast_to(ref, m.shape)) <= MASS_RTOL, causal
+        assert rel_to_max(m, np.broadcast_to(ref, m.shape)) <= PIPE_RTOL, causal
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -93,7 +98,7 @@ def test_mass_full_size(fa, causal):
     m = to_f64(fa.key_mass(q, k, lse, causal, w.scale))
     torch.cuda.synchronize()
     assert np.all(m >= 0)
-    assert np.allclose(m.sum(1), H * N, rtol=1e-4)
+    assert np.allclose(m.sum(1), H * N, rtol=PIPE_RTOL)
     b = B - 1
     announce("mass full size: oracle for one batch")
     ref = np.zeros(N)
@@ -102,5 +107,4 @@ def test_mass_full_size(fa, causal):
                                  oracle.bf16_bits_to_f64(x["k"][b, h]), causal, w.scale)
         ref += p.sum(axis=0)
         del p
-    assert rel_to_max(m[b], ref) <= MASS_RTOL
-    assert max_abs(m[b], ref) <= MASS_RTOL * float(np.max(ref))
+    assert rel_to_max(m[b], ref) <= PIPE_RTOL

@@ -127,9 +127,9 @@ def test_side_stream(fa):
 
 # --- full-size workloads --------------------------------------------------------
 
-def _sample_heads(B, H, n, seed):
+def _sample_heads(B, H, n, seed, always=()):
     rng = np.random.default_rng(seed)
-    heads = {(0, 0), (B - 1, H - 1)}
+    heads = {(0, 0), (B - 1, H - 1), *always}
     while len(heads) < min(n, B * H):
         heads.add((int(rng.integers(B)), int(rng.integers(H))))
     return sorted(heads)
@@ -142,7 +142,10 @@ def _check_workload(fa, wname):
     x = ai.make_inputs(w)
     B, H, N, d = w.B, w.H, w.N, w.d
     small = B * H * N * N <= 4 * 32 * 1024 * 1024  # whole-tensor oracle is cheap
-    heads = [(b, h) for b in range(B) for h in range(H)] if small else _sample_heads(B, H, 6, w.seed)
+    # (0, 40) of the 4x64x4096x128 inputs holds the rows with the largest
+    # rounding error of the forward (found by a CPU model of its arithmetic)
+    heads = [(b, h) for b in range(B) for h in range(H)] if small else \
+        _sample_heads(B, H, 12, w.seed, always=[(0, 40)] if wname == "c5" else [])
     rng = np.random.default_rng(100 + w.seed)
     for causal in w.causal_modes:
         announce(f"workload {wname} causal={causal} on GPU")
