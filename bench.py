@@ -196,6 +196,21 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         mass_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+    # the FP8 forward (Q, K quantised per 16 x 16 block), bf16 inputs only
+    fp8_ms = None
+    if args.dtype == "bf16":
+        o8 = torch.empty_like(q)
+        l8 = torch.empty_like(lse)
+        fa.forward_fp8(q, k, v, causal, w.scale, out=o8, lse=l8)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in fev:
+            e0.record(stream)
+            fa.forward_fp8(q, k, v, causal, w.scale, out=o8, lse=l8)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        fp8_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
+        del o8, l8
 
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if not args.fwd_only else [0.0]
@@ -223,6 +238,9 @@ def main():
     # S = Q K^T is the pass's only product: half the forward's FLOPs
     r_mass = roof("fa_key_mass", "key_mass_kernel + key_mass_reduce_kernel", f_fwd / 2, mass_ms) \
         if mass_ms is not None else None
+    # its products run on bf16 matrix cores (the dequantised operands are exact in bf16)
+    r_fp8 = roof("fa_fwd_fp8", "quant_e4m3_kernel x2 + fwd_kernel", f_fwd, fp8_ms) \
+        if fp8_ms is not None else None
 
     out = {
         "metric": "bf16 attention TFLOP/s fwd & fwd+bwd at 4x64x4096x128 causal, % MFMA peak",
@@ -251,6 +269,7 @@ def main():
         "roofline": roofline,
         "roofline_fwd": r_fwd,
         "roofline_key_mass": r_mass,
+        "roofline_fwd_fp8": r_fp8,
         "cpu_baseline": None,
     }
     if hkv != w.H:
