@@ -30,33 +30,39 @@ __device__ __forceinline__ float e4m3_byte(uint32_t w, int b) {
   }
 }
 
-// One wave per (head, 16-row block): lane l holds row 16 rb + l / 4 and
-// D / 4 consecutive columns starting at (l % 4) D / 4, i.e. one (d = 64) or
-// two (d = 128) 16-column blocks; the 16 lanes sharing l % 4 hold the 16 rows
-// of the same blocks. Loads and stores are 16-byte vectors, four lanes per
-// row, rows consecutive: fully coalesced.
+// One wave per (matrix, 16-row block). The block's rows are consecutive in
+// memory (16 D 2 bytes), so instruction v of the wave moves bytes
+// [1024 v, 1024 v + 1024) of it: lane l takes the 16-byte chunk l % CPR of
+// row v RPI + l / CPR (CPR = D / 8 chunks per row, RPI = 64 / CPR rows per
+// instruction). Every load and store instruction is one contiguous span. A
+// lane's chunks all lie in 16-column block (l % CPR) / 2, and the lanes of one
+// block differ in bit 0 and in the bits from CPR up: a 3- or 4-step XOR
+// shuffle gives the block's amax.
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void quant_e4m3_kernel(const __bf16* __restrict__ X,
                                                          uint8_t* __restrict__ codes,
                                                          float* __restrict__ scales,
                                                          __bf16* __restrict__ deq, int N,
                                                          long long nblk) {
-  constexpr int EL = D / 4;   // elements per lane
-  constexpr int NC = EL / 16; // 16-column blocks per lane
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per instruction
+  constexpr int NI = 16 / RPI;    // instructions per block
+  constexpr int EL = 8 * NI;      // elements per lane
   const long long wb = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wb >= nblk) return;     // whole waves only
+  if (wb >= nblk) return;         // whole waves only
   const int lane = threadIdx.x & 63;
   const int nrb = (N + 15) / 16;
   const long long r = wb / nrb;
   const int rb = (int)(wb - r * nrb);
-  const int row = rb * 16 + (lane >> 2);
-  const bool valid = row < N;
-  const size_t off = ((size_t)r * N + (valid ? row : 0)) * D + (lane & 3) * EL;
+  const int rows = min(16, N - 16 * rb);  // rows of this block (the last may be short)
+  const int c = lane % CPR;               // chunk of the row
+  const size_t blk0 = ((size_t)r * N + 16 * rb) * D;  // first element of the block
 
   float x[EL];
 #pragma unroll
-  for (int v = 0; v < EL / 8; ++v) {
-    u32x4 w = valid ? ld_global16(X + off + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+  for (int v = 0; v < NI; ++v) {
+    const int rr = v * RPI + lane / CPR;
+    const u32x4 w = rr < rows ? ld_global16(X + blk0 + (size_t)rr * D + 8 * c) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       x[8 * v + 2 * m] = lo16<F16>(w[m]);
@@ -64,31 +70,27 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const __bf16* __restric
     }
   }
 
-  int e[NC];
+  float amax = 0.f;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    float amax = 0.f;
+  for (int i = 0; i < EL; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[16 * c + i]));
-#pragma unroll
-    for (int s = 4; s < 64; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s));
-    // amax = m 2^E, m in [0.5, 1); 448 = 0.875 2^9
-    const float m = __builtin_amdgcn_frexp_mantf(amax);
-    const int E = __builtin_amdgcn_frexp_expf(amax);
-    int ec = m <= 0.875f ? E - 9 : E - 8;
-    ec = ec < -100 ? -100 : ec;
-    e[c] = amax == 0.f ? 0 : ec;
-  }
+  for (int sh = CPR; sh < 64; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+  // amax = m 2^E, m in [0.5, 1); 448 = 0.875 2^9
+  const float mant = __builtin_amdgcn_frexp_mantf(amax);
+  const int E = __builtin_amdgcn_frexp_expf(amax);
+  int e = mant <= 0.875f ? E - 9 : E - 8;
+  e = e < -100 ? -100 : e;
+  e = amax == 0.f ? 0 : e;
 
   uint32_t cw[EL / 4];  // codes, 4 per dword
 #pragma unroll
   for (int j = 0; j < EL / 4; ++j) {
-    const int c = (4 * j) / 16;
     const float* y4 = &x[4 * j];
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(y4[0], -e[c]),
-                                            __builtin_amdgcn_ldexpf(y4[1], -e[c]), 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(y4[2], -e[c]),
-                                        __builtin_amdgcn_ldexpf(y4[3], -e[c]), w, true);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(y4[0], -e),
+                                            __builtin_amdgcn_ldexpf(y4[1], -e), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(y4[2], -e),
+                                        __builtin_amdgcn_ldexpf(y4[3], -e), w, true);
     uint32_t u = (uint32_t)w;
     // zero is +0: clear the sign of every byte whose magnitude bits are 0
 #pragma unroll
@@ -97,34 +99,28 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const __bf16* __restric
     cw[j] = u;
   }
 
-  if (valid && codes != nullptr) {
 #pragma unroll
-    for (int v = 0; v < EL / 16; ++v)
-      *reinterpret_cast<u32x4*>(codes + off + 16 * v) =
-          u32x4{cw[4 * v], cw[4 * v + 1], cw[4 * v + 2], cw[4 * v + 3]};
-  }
-  if (valid && deq != nullptr) {
-    // decode(code) * 2^e has at most 4 significant bits and a normal
-    // exponent: exact in bf16, so its top 16 bits are the bf16 value
-#pragma unroll
-    for (int v = 0; v < EL / 8; ++v) {
+  for (int v = 0; v < NI; ++v) {
+    const int rr = v * RPI + lane / CPR;
+    if (rr >= rows) continue;
+    const size_t off = blk0 + (size_t)rr * D + 8 * c;
+    if (codes != nullptr) *reinterpret_cast<u32x2*>(codes + off) = u32x2{cw[2 * v], cw[2 * v + 1]};
+    if (deq != nullptr) {
+      // decode(code) * 2^e has at most 4 significant bits and a normal
+      // exponent: exact in bf16, so its top 16 bits are the bf16 value
       u32x4 o;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int i = 8 * v + 2 * m;  // elements i, i + 1 in dword i / 4, bytes i % 4, i % 4 + 1
-        const int c = i / 16;
-        const float a = __builtin_amdgcn_ldexpf(e4m3_byte(cw[i / 4], i % 4), e[c]);
-        const float b = __builtin_amdgcn_ldexpf(e4m3_byte(cw[i / 4], i % 4 + 1), e[c]);
+        const int i = 8 * v + 2 * m;  // elements i, i + 1: dword i / 4, bytes i % 4, i % 4 + 1
+        const float a = __builtin_amdgcn_ldexpf(e4m3_byte(cw[i / 4], i % 4), e);
+        const float b = __builtin_amdgcn_ldexpf(e4m3_byte(cw[i / 4], i % 4 + 1), e);
         o[m] = (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
       }
-      *reinterpret_cast<u32x4*>(deq + off + 8 * v) = o;
+      *reinterpret_cast<u32x4*>(deq + off) = o;
     }
   }
-  if (scales != nullptr && lane < 4) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      scales[((size_t)r * nrb + rb) * (D / 16) + lane * NC + c] = __builtin_amdgcn_ldexpf(1.f, e[c]);
-  }
+  if (scales != nullptr && lane < CPR && (lane & 1) == 0)
+    scales[((size_t)r * nrb + rb) * (D / 16) + lane / 2] = __builtin_amdgcn_ldexpf(1.f, e);
 }
 
 template <int D, bool F16>
