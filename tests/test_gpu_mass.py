@@ -63,6 +63,27 @@ def test_mass_small_every_key(fa, H, Hkv, N, causal, d):
     assert np.allclose(to_f64(m2).sum(1), H * N, rtol=PIPE_RTOL)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [33, 300])
+def test_mass_f16(fa, N, causal):
+    """IEEE binary16 inputs, grouped K/V heads, the oracle's LSE fed in."""
+    import torch
+    B, H, Hkv, d = 2, 4, 2, 128
+    seed = 8600 + N + int(causal)
+    x = ai.make_qkv(B, H, N, d, seed, Hkv=Hkv, dtype="f16")
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    announce(f"mass f16 N={N} causal={causal} seed={seed}")
+    f = {n: oracle.f16_bits_to_f64(b) for n, b in x.items()}
+    ref = oracle.key_mass(f["q"], f["k"], causal, scale)
+    _, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal, scale)
+    q, k = (torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).cuda().view(torch.float16)
+            for n in ("q", "k"))
+    m = fa.key_mass(q, k, torch.from_numpy(lse_ref.astype(np.float32)).cuda(), causal, scale)
+    torch.cuda.synchronize()
+    assert rel_to_max(to_f64(m), ref) <= MASS_RTOL
+    assert np.allclose(to_f64(m).sum(1), H * N, rtol=1e-4)
+
+
 def test_mass_identical_keys_closed_form(fa):
     """All keys equal: P is uniform over the visible keys, so key j gets mass
     H (non-causal) or H sum_{i >= j} 1 / (i + 1) (causal)."""
