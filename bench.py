@@ -71,6 +71,41 @@ def stored_traffic(launch: str):
     return t.get("bytes_per_launch", {}).get(launch)
 
 
+def time_stats(ms):
+    """Median, min and 90th percentile of per-launch times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def parse_dpm_levels(text):
+    """Engine-clock levels (MHz) from a pp_dpm_sclk listing ("0: 500Mhz *")."""
+    out = []
+    for line in text.splitlines():
+        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+        if m:
+            out.append(int(m.group(1)))
+    return out
+
+
+def reported_peak(cus):
+    """bf16 dense matrix-core peak at the highest engine clock the driver lists:
+    CUs x 4096 FLOP per clock (4 SIMDs x one 32x32x16 product, 32768 FLOP, per
+    32 cycles each). Returns (peak TFLOP/s, clock MHz, source) or Nones."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                levels = parse_dpm_levels(f.read())
+        except OSError:
+            continue
+        if levels:
+            mhz = max(levels)
+            return cus * 4096 * mhz * 1e6 / 1e12, mhz, path
+    return None, None, None
+
+
 def flops(w, causal):
     f = 4.0 * w.B * w.H * w.N * w.N * w.d
     if causal:
@@ -225,11 +260,16 @@ def main():
 
     def roof(launch, kernels, fl, tms):
         achieved = fl / (tms * 1e-3) / 1e12
-        return {"bound": "mfma", "kernel": f"{launch} ({kernels})", "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(launch) if default_launch else None,
-                "avg_launch_ms": round(tms, 4)}
+        traffic = stored_traffic(launch) if default_launch else None
+        r = {"bound": "mfma", "kernel": f"{launch} ({kernels})", "achieved": round(achieved, 2),
+             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+             "traffic": traffic,
+             "avg_launch_ms": round(tms, 4)}
+        if traffic is not None:  # measured HBM bytes per launch over this launch time
+            r["hbm_gbs"] = round(traffic / (tms * 1e-3) / 1e9, 1)
+            r["hbm_frac"] = round(traffic / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        return r
 
     r_fwd = roof("fa_fwd", "fwd_kernel", f_fwd, t_fwd)
     r_bwd = roof("fa_bwd", "bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel", f_bwd, t_bwd) \
@@ -261,6 +301,8 @@ def main():
                    "fwd_only": args.fwd_only},
         "fwd_ms": round(t_fwd, 4),
         "bwd_ms": round(t_bwd, 4),
+        "fwd_ms_stats": time_stats(fwd_ms),
+        "bwd_ms_stats": time_stats(bwd_ms),
         "fwd_tflops": round(fwd_tf, 2),
         "bwd_tflops": round(bwd_tf, 2),
         "fwd_pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
@@ -272,6 +314,14 @@ def main():
         "roofline_fwd_fp8": r_fp8,
         "cpu_baseline": None,
     }
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    pk, mhz, src = reported_peak(cus)
+    out["peak_at_reported_clock"] = {
+        "tflops": round(pk, 1) if pk else None, "sclk_mhz": mhz, "cus": cus, "source": src,
+        "fwd_frac": round(fwd_tf / pk, 4) if pk else None,
+        "note": "bf16 dense matrix-core peak recomputed as CUs x 4096 FLOP/clock at the highest "
+                "engine clock the driver lists; `peak` in the roofline objects is the published "
+                "2.5 PFLOP/s"}
     if hkv != w.H:
         out["config"]["workload"] += f", {hkv} K/V heads"
         out["config"]["Hkv"] = hkv

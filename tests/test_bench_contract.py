@@ -35,3 +35,15 @@ def test_stored_traffic_follows_source_hash(tmp_path, monkeypatch):
     assert bench.stored_traffic("fa_fwd") == 123
     path.write_text(json.dumps({"source_sha256": "0" * 64, "bytes_per_launch": {"fa_fwd": 123}}))
     assert bench.stored_traffic("fa_fwd") is None  # kernels changed since
+
+
+def test_time_stats():
+    st = bench.time_stats([4.0, 1.0, 3.0, 2.0, 10.0])
+    assert st == {"median": 3.0, "min": 1.0, "p90": 7.6}
+
+
+def test_dpm_levels_and_peak_formula():
+    assert bench.parse_dpm_levels("0: 500Mhz \n1: 1600Mhz *\n2: 2400Mhz\n") == [500, 1600, 2400]
+    assert bench.parse_dpm_levels("no clocks here") == []
+    # 256 CUs x 4096 FLOP per clock at 2.4 GHz: the 2.517 PFLOP/s behind the published 2.5
+    assert abs(256 * 4096 * 2400e6 / 1e12 - 2516.6) < 0.1
