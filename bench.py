@@ -272,7 +272,7 @@ def main():
         return r
 
     r_fwd = roof("fa_fwd", "fwd_kernel", f_fwd, t_fwd)
-    r_bwd = roof("fa_bwd", "bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel", f_bwd, t_bwd) \
+    r_bwd = roof("fa_bwd", "bwd_dq_kernel + bwd_dkdv_kernel", f_bwd, t_bwd) \
         if not args.fwd_only else None
     roofline = r_bwd if (r_bwd is not None and t_bwd >= t_fwd) else r_fwd
     # S = Q K^T is the pass's only product: half the forward's FLOPs

@@ -2,10 +2,14 @@
 //
 // The probabilities are recomputed from the stored log-sum-exp rather than
 // kept ("GPU Performance Optimization Batch 1 - Design Spec", Item 3, Design,
-// backward file). Three launches on one stream:
+// backward file). Two launches on one stream (three with the dK/dV split):
 //
-//  1. bwd_pre_kernel: per query row, D_i = dO_i . O_i (float32) and the LSE in
-//     base 2, as two planes.
+//  1. bwd_dq_kernel: one workgroup per (batch, head, query tile), sweeping key
+//     tiles like the forward (and with its two-group schedule): S and dP are
+//     recomputed and dQ += dS K is summed in registers, so dQ needs no atomics
+//     and no float32 scratch. It first forms its rows' statistics, D_i =
+//     dO_i . O_i (float32) and the LSE in base 2, and stores them as two
+//     planes for the next pass.
 //  2. bwd_dkdv_kernel: one workgroup per (batch, head, block of 128 keys); each
 //     32-key block has a P-wave (dV) and a dS-wave (dK) on one SIMD, holding
 //     float32 accumulators for the whole sweep over query tiles of 64 rows,
@@ -17,10 +21,8 @@
 //        P = exp2(c S - LSE2), dS = P (dP - D)
 //        dV += P^T dO, dK += dS^T Q    (P^T, dS^T straight from registers)
 //     Causal: query tiles that see none of the block's keys are skipped.
-//  3. bwd_dq_kernel: one workgroup per (batch, head, query tile), sweeping key
-//     tiles like the forward (and with its two-group schedule): S and dP are
-//     recomputed and dQ += dS K is summed in registers, so dQ needs no atomics
-//     and no float32 scratch.
+//  (3. bwd_reduce_kernel, only when the dK/dV work of few K/V heads is split
+//     over several workgroups: sums their float32 partials.)
 //
 // The pages' backward gathers dQ with atomic updates ("RTX Flash Attention
 // Implementation COMPLETE", CUDA Kernel Design, backward kernel); on MI355X the
@@ -38,37 +40,7 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// 1. Row statistics
-// ---------------------------------------------------------------------------
-template <int D, bool F16>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
-                                                     const __bf16* __restrict__ dO,
-                                                     const float* __restrict__ LSE,
-                                                     float* __restrict__ rowstat, long long rows) {
-  constexpr int CH = D / 8;  // lanes per row
-  const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = gt / CH;
-  const int c = (int)(gt % CH);
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = ld_global16(O + row * D + 8 * c);
-    const u32x4 b = ld_global16(dO + row * D + 8 * c);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      acc += lo16<F16>(a[m]) * lo16<F16>(b[m]);
-      acc += hi16<F16>(a[m]) * hi16<F16>(b[m]);
-    }
-  }
-#pragma unroll
-  for (int off = CH / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, CH);
-  if (row < rows && c == 0) {
-    rowstat[row] = LSE[row] * kLog2e;  // LSE in base 2
-    rowstat[rows + row] = acc;         // D
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dK/dV kernel
+// dK/dV kernel
 // ---------------------------------------------------------------------------
 template <int D>
 struct BwdCfg {
@@ -460,7 +432,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ kernel
+// dQ kernel
 // ---------------------------------------------------------------------------
 // One workgroup per (batch, head, tile of 256 queries); each of its 8 waves
 // owns 32 query rows and sweeps the key tiles like the forward kernel, with
@@ -470,7 +442,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
 //   dQ^T += K_j^T dS^T                 (dS^T straight from registers; K_j^T
 //                                       by transposing reads of the K tile)
 // and writes dQ = scale * dQ^T as bf16. No atomics: each dQ row is summed
-// over all keys inside one wave.
+// over all keys inside one wave. Before the sweep each lane forms its row's
+// statistics (D = dO . O from the dO^T operand it holds and the O row, and
+// the LSE in base 2), which it uses itself and stores for the dK/dV pass: this
+// pass runs first, and no separate statistics pass reads O and dO again.
 // The schedule is the forward's two-group ping-pong: a wave alternates
 //   M(t): dQ^T += K_t^T dS^T_t, then S^T_{t+1}, dP^T_{t+1}   (matrix cores)
 //   V(t): dS^T_t from S^T_t, dP^T_t                          (vector ALUs)
@@ -493,7 +468,8 @@ template <int D, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                   const float* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
+                   const __bf16* __restrict__ O, const float* __restrict__ LSE,
+                   float* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
                    int G, float c_log2, float scale) {
   // BH query heads; query head bh reads K/V head bh / G
   using C = DqCfg<D>;
@@ -532,9 +508,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rK = make_rsrc(K + kvhead, head_bytes);
   const auto rV = make_rsrc(V + kvhead, head_bytes);
   const auto rdO = make_rsrc(dO + head, head_bytes);
-  // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
-  const auto rL2 = make_rsrc(rowstat + (size_t)bh * N, (uint32_t)N * 4u);
-  const auto rDD = make_rsrc(rowstat + (size_t)BH * N + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rO = make_rsrc(O + head, head_bytes);
+  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * rblk;
@@ -546,16 +521,31 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // last key tile this wave needs (-1: none)
   const int jw_last = !wave_active ? -1 : CAUSAL ? min(wrow0 + 31, N - 1) / BC : T - 1;
 
-  // Q^T and dO^T operands (rows past N read as zeros) and the row statistics
+  // Q^T and dO^T operands (rows past N read as zeros), and the row statistics:
+  // the LSE in base 2, and D = dO . O (the lane's half of the row, then its
+  // partner's). This pass runs first and stores both for the dK/dV pass.
   bf16x8 qf[D / 16], of[D / 16];
+  float dacc = 0.f;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const uint32_t off = (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2;
     qf[s] = as_bf16x8(buf_load16(rQ, off));
     of[s] = as_bf16x8(buf_load16(rdO, off));
+    const u32x4 ow = buf_load16(rO, off), dw = as_u32x4(of[s]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      dacc += lo16<F16>(ow[m]) * lo16<F16>(dw[m]);
+      dacc += hi16<F16>(ow[m]) * hi16<F16>(dw[m]);
+    }
   }
-  const float neg_l2 = -__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL2, (uint32_t)row * 4u, 0, 0));
-  const float dval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rDD, (uint32_t)row * 4u, 0, 0));
+  const float dval = pair_sum(dacc);
+  const float l2 =
+      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, (uint32_t)row * 4u, 0, 0)) * kLog2e;
+  const float neg_l2 = -l2;
+  if (hh == 0 && row < N) {
+    rowstat[(size_t)bh * N + row] = l2;                     // LSE in base 2
+    rowstat[(size_t)BH * N + (size_t)bh * N + row] = dval;  // D
+  }
 
   // ---- tile loads, straight from HBM into LDS: instruction n of a tile fills
   // chunk positions [64 n, 64 n + 64); each lane fetches the chunk the layout
@@ -777,14 +767,17 @@ template <int D, bool CAUSAL, bool F16>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   using C = BwdCfg<D>;
   using Cq = DqCfg<D>;
-  const long long rows = (long long)a.B * a.H * a.N;
   float* rowstat = a.rowstat;
   const float c_log2 = a.softmax_scale * kLog2e;
   {
-    const long long threads = rows * (D / 8);
-    const hipError_t e = launch_kernel(bwd_pre_kernel<D, F16>, dim3((unsigned)((threads + 255) / 256)),
-                                       dim3(256), a.stream, (const __bf16*)a.O, (const __bf16*)a.dO,
-                                       a.LSE, rowstat, rows);
+    // dQ pass first: it also writes the row statistics the dK/dV pass reads
+    const int nq = (a.N + Cq::BR - 1) / Cq::BR;
+    const long long total = (long long)nq * a.B * a.H;
+    const hipError_t e = launch_kernel(
+        bwd_dq_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(Cq::THREADS), a.stream,
+        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
+        (const __bf16*)a.O, a.LSE, rowstat, (__bf16*)a.dQ, a.N, a.B * a.H, a.H / a.Hkv, c_log2,
+        a.softmax_scale);
     if (e != hipSuccess) return e;
   }
   {
@@ -808,14 +801,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
       if (r != hipSuccess) return r;
     }
   }
-  {
-    const int nq = (a.N + Cq::BR - 1) / Cq::BR;
-    const long long total = (long long)nq * a.B * a.H;
-    return launch_kernel(bwd_dq_kernel<D, CAUSAL, F16>, dim3((unsigned)total),
-                         dim3(Cq::THREADS), a.stream, (const __bf16*)a.Q, (const __bf16*)a.K,
-                         (const __bf16*)a.V, (const __bf16*)a.dO, (const float*)rowstat,
-                         (__bf16*)a.dQ, a.N, a.B * a.H, a.H / a.Hkv, c_log2, a.softmax_scale);
-  }
+  return hipSuccess;
 }
 
 template <bool F16>
