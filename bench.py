@@ -279,7 +279,7 @@ def main():
     r_mass = roof("fa_key_mass", "key_mass_kernel + key_mass_reduce_kernel", f_fwd / 2, mass_ms) \
         if mass_ms is not None else None
     # its products run on bf16 matrix cores (the dequantised operands are exact in bf16)
-    r_fp8 = roof("fa_fwd_fp8", "quant_e4m3_kernel x2 + fwd_kernel", f_fwd, fp8_ms) \
+    r_fp8 = roof("fa_fwd_fp8", "quant_e4m3_kernel (K) + fwd_kernel (Q quantised on load)", f_fwd, fp8_ms) \
         if fp8_ms is not None else None
 
     out = {

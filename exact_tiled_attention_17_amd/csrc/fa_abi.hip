@@ -138,19 +138,20 @@ int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
   if (LSE != nullptr && !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const size_t q_bytes = (size_t)B * H * N * d * 2, k_bytes = (size_t)B * Hkv * N * d * 2;
-  void* scratch = nullptr;  // dequantised Q, then K (bf16)
-  const hipError_t m = hipMallocAsync(&scratch, q_bytes + k_bytes, s);
+  // K is quantised into scratch (it reaches the forward's LDS tiles by direct
+  // loads); Q is quantised by the forward itself as it loads its operands
+  const size_t k_bytes = (size_t)B * Hkv * N * d * 2;
+  void* scratch = nullptr;  // dequantised K (bf16)
+  const hipError_t m = hipMallocAsync(&scratch, k_bytes, s);
   if (m != hipSuccess || scratch == nullptr)
     return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
-  char* qd = static_cast<char*>(scratch);
-  char* kd = qd + q_bytes;
-  hipError_t e = fa::launch_quant(fa::QuantArgs{Q, nullptr, nullptr, qd, B * H, N, d, s, false});
-  if (e == hipSuccess)
-    e = fa::launch_quant(fa::QuantArgs{K, nullptr, nullptr, kd, B * Hkv, N, d, s, false});
-  if (e == hipSuccess)
-    e = fa::launch_fwd(fa::FwdArgs{qd, kd, V, O, LSE, B, H, N, d, causal != 0, softmax_scale, s,
-                                   false, Hkv});
+  char* kd = static_cast<char*>(scratch);
+  hipError_t e = fa::launch_quant(fa::QuantArgs{K, nullptr, nullptr, kd, B * Hkv, N, d, s, false});
+  if (e == hipSuccess) {
+    fa::FwdArgs fa_args{Q, kd, V, O, LSE, B, H, N, d, causal != 0, softmax_scale, s, false, Hkv};
+    fa_args.quant_q = true;
+    e = fa::launch_fwd(fa_args);
+  }
   const hipError_t f = hipFreeAsync(scratch, s);
   return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
 }

@@ -47,6 +47,49 @@ __device__ __forceinline__ f32x16 mfma32x(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// ---- E4M3 (OCP FP8: bias 7, largest finite 448) block quantisation ---------
+// The scale of a block with largest magnitude amax is 2^e with the smallest e
+// for which amax <= 448 2^e, e >= -100, and e = 0 for a zero block. Then
+// nothing saturates and every dequantised value decode(code) 2^e has at most
+// 4 significant bits and a normal exponent, so it is exact in bf16.
+__device__ __forceinline__ int e4m3_block_exp(float amax) {
+  // amax = m 2^E, m in [0.5, 1); 448 = 0.875 2^9
+  const float mant = __builtin_amdgcn_frexp_mantf(amax);
+  const int E = __builtin_amdgcn_frexp_expf(amax);
+  int e = mant <= 0.875f ? E - 9 : E - 8;
+  e = e < -100 ? -100 : e;
+  return amax == 0.f ? 0 : e;
+}
+// Codes of x0..x3 / 2^e (the E4M3 value nearest, ties to even), byte i for
+// x_i; a code of magnitude zero is +0.
+__device__ __forceinline__ uint32_t e4m3_codes4(float x0, float x1, float x2, float x3, int e) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x0, -e),
+                                          __builtin_amdgcn_ldexpf(x1, -e), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x2, -e),
+                                      __builtin_amdgcn_ldexpf(x3, -e), w, true);
+  uint32_t u = (uint32_t)w;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if (((u >> (8 * b)) & 0x7Fu) == 0u) u &= ~(0xFFu << (8 * b));
+  return u;
+}
+// Byte b (0..3) of w decoded from E4M3 (the byte selector must be a constant).
+__device__ __forceinline__ float e4m3_byte(uint32_t w, int b) {
+  switch (b) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  }
+}
+// Bytes b, b + 1 of codes w dequantised at scale 2^e, as a packed bf16 pair
+// (exact: the top halves of the float32 values).
+__device__ __forceinline__ uint32_t e4m3_deq2_bf16(uint32_t w, int b, int e) {
+  const float a = __builtin_amdgcn_ldexpf(e4m3_byte(w, b), e);
+  const float c = __builtin_amdgcn_ldexpf(e4m3_byte(w, b + 1), e);
+  return (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, c) & 0xFFFF0000u);
+}
+
 // Lanes l and l ^ 32 exchange values; returns (own, partner) in some order,
 // so symmetric reductions (max, sum) over the pair are exact either way.
 __device__ __forceinline__ float pair_max(float x) {

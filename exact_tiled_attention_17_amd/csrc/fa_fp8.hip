@@ -1,6 +1,8 @@
 // FP8 (E4M3) path: Q and K quantised per 16 x 16 block before S = Q K^T
 // ("GPU Performance Optimization Batch 1 - Design Spec", Item 3, Design,
 // optional FP8 path; Item 2, Design, Step 1 for the saturating E4M3 cast).
+// This file holds the quantisation kernel (fa_quantize_e4m3, and K for
+// fa_fwd_fp8); the forward quantises Q itself as it loads it (fa_fwd.hip).
 //
 // A block is 16 token rows x 16 head-dim columns of one head. Its scale is
 // the power of two 2^e with the smallest e such that the block's largest
@@ -19,16 +21,6 @@
 #include "fa_launch.h"
 
 namespace fa {
-
-// Byte b (0..3) of w decoded from E4M3 (the byte selector must be a constant).
-__device__ __forceinline__ float e4m3_byte(uint32_t w, int b) {
-  switch (b) {
-    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
-    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
-    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
-  }
-}
 
 // One wave per (matrix, 16-row block). The block's rows are consecutive in
 // memory (16 D 2 bytes), so instruction v of the wave moves bytes
@@ -76,28 +68,11 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const __bf16* __restric
   amax = fmaxf(amax, __shfl_xor(amax, 1));
 #pragma unroll
   for (int sh = CPR; sh < 64; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
-  // amax = m 2^E, m in [0.5, 1); 448 = 0.875 2^9
-  const float mant = __builtin_amdgcn_frexp_mantf(amax);
-  const int E = __builtin_amdgcn_frexp_expf(amax);
-  int e = mant <= 0.875f ? E - 9 : E - 8;
-  e = e < -100 ? -100 : e;
-  e = amax == 0.f ? 0 : e;
+  const int e = e4m3_block_exp(amax);
 
   uint32_t cw[EL / 4];  // codes, 4 per dword
 #pragma unroll
-  for (int j = 0; j < EL / 4; ++j) {
-    const float* y4 = &x[4 * j];
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(y4[0], -e),
-                                            __builtin_amdgcn_ldexpf(y4[1], -e), 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(y4[2], -e),
-                                        __builtin_amdgcn_ldexpf(y4[3], -e), w, true);
-    uint32_t u = (uint32_t)w;
-    // zero is +0: clear the sign of every byte whose magnitude bits are 0
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (((u >> (8 * b)) & 0x7Fu) == 0u) u &= ~(0xFFu << (8 * b));
-    cw[j] = u;
-  }
+  for (int j = 0; j < EL / 4; ++j) cw[j] = e4m3_codes4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], e);
 
 #pragma unroll
   for (int v = 0; v < NI; ++v) {
@@ -112,9 +87,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const __bf16* __restric
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int i = 8 * v + 2 * m;  // elements i, i + 1: dword i / 4, bytes i % 4, i % 4 + 1
-        const float a = __builtin_amdgcn_ldexpf(e4m3_byte(cw[i / 4], i % 4), e);
-        const float b = __builtin_amdgcn_ldexpf(e4m3_byte(cw[i / 4], i % 4 + 1), e);
-        o[m] = (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
+        o[m] = e4m3_deq2_bf16(cw[i / 4], i % 4, e);
       }
       *reinterpret_cast<u32x4*>(deq + off) = o;
     }

@@ -87,7 +87,9 @@ __device__ __forceinline__ int voff(int r, int col) {  // element offset of (r, 
 // every SIMD one wave's softmax runs while the other wave's products do.
 // Query rows are dealt in 32-row blocks alternating between the groups, so both
 // reach the causal diagonal on the same key tile.
-template <int D, bool CAUSAL, bool F16>
+// QQ: the FP8 path's Q, quantised to E4M3 per 16 x 16 block (scale rule in
+// fa_common.h) and dequantised in registers as it is loaded (bf16 only).
+template <int D, bool CAUSAL, bool F16, bool QQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -152,6 +154,35 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
     qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
+  if constexpr (QQ) {
+    // A 16 x 16 block of Q is 16 rows (lanes l32 in one half of 0..31; wave
+    // rows start at multiples of 32, block rows at multiples of 16) by 16
+    // columns (k-step s, both half-waves): its amax takes a 5-step XOR
+    // reduction over lane bits 0..3 and 5. Rows past N read as zeros, as in
+    // the short last block of the quantisation kernel.
+    static_assert(!(QQ && F16), "the FP8 path takes bf16 inputs");
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 w = as_u32x4(qf[s]);
+      float x[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        x[2 * m] = lo16<false>(w[m]);
+        x[2 * m + 1] = hi16<false>(w[m]);
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+      for (int sh = 1; sh < 16; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const int e = e4m3_block_exp(amax);
+      const uint32_t c0 = e4m3_codes4(x[0], x[1], x[2], x[3], e);
+      const uint32_t c1 = e4m3_codes4(x[4], x[5], x[6], x[7], e);
+      qf[s] = as_bf16x8(u32x4{e4m3_deq2_bf16(c0, 0, e), e4m3_deq2_bf16(c0, 2, e),
+                              e4m3_deq2_bf16(c1, 0, e), e4m3_deq2_bf16(c1, 2, e)});
+    }
+  }
 
   // ---- K/V tiles, straight from HBM into LDS: instruction n of a tile fills
   // the 64 consecutive 16-byte chunk positions [64 n, 64 n + 64) of the tile's
@@ -409,24 +440,26 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     LSE[(size_t)bh * N + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool F16>
+template <int D, bool CAUSAL, bool F16, bool QQ>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdCfg<D>;
   const int nq = (a.N + C::BR - 1) / C::BR;
   const long long total = (long long)nq * a.B * a.H;
-  return launch_kernel(fwd_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+  return launch_kernel(fwd_kernel<D, CAUSAL, F16, QQ>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
                        a.LSE, a.N, a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e);
 }
 
-template <bool F16>
+template <bool F16, bool QQ>
 static hipError_t launch_fwd_dt(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_fwd_t<128, true, F16>(a) : launch_fwd_t<128, false, F16>(a);
-  return a.causal ? launch_fwd_t<64, true, F16>(a) : launch_fwd_t<64, false, F16>(a);
+  if (a.d == 128)
+    return a.causal ? launch_fwd_t<128, true, F16, QQ>(a) : launch_fwd_t<128, false, F16, QQ>(a);
+  return a.causal ? launch_fwd_t<64, true, F16, QQ>(a) : launch_fwd_t<64, false, F16, QQ>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  return a.f16 ? launch_fwd_dt<true>(a) : launch_fwd_dt<false>(a);
+  if (a.quant_q) return a.f16 ? hipErrorInvalidValue : launch_fwd_dt<false, true>(a);
+  return a.f16 ? launch_fwd_dt<true, false>(a) : launch_fwd_dt<false, false>(a);
 }
 
 }  // namespace fa

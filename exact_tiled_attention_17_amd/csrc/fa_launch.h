@@ -19,6 +19,7 @@ struct FwdArgs {
   hipStream_t stream;
   bool f16;  // element type of Q, K, V, O: IEEE binary16 (true) or bf16
   int Hkv;   // K/V heads; divides H (query head h reads K/V head h / (H / Hkv))
+  bool quant_q = false;  // FP8 path: quantise Q to E4M3 per 16 x 16 block on load (bf16 only)
 };
 
 struct BwdArgs {

@@ -222,9 +222,9 @@ int fa_quantize_e4m3(const void* X, void* codes, float* scales, int R, int N,
  * errors as fa_fwd_ex with dtype bf16 (the only element type of this path;
  * there is no FP8 backward). The dequantised values have at most 4
  * significant bits, so the bf16 matrix products use them exactly. Inputs must
- * be finite with magnitudes below 2^120. Takes 2*(B*H + B*Hkv)*N*d bytes of
- * scratch (the dequantised Q and K), stream-ordered like fa_bwd's;
- * FA_ERR_OUT_OF_MEMORY if it cannot be had.
+ * be finite with magnitudes below 2^120. Takes 2*B*Hkv*N*d bytes of scratch
+ * (the dequantised K; Q is quantised as the forward loads it), stream-ordered
+ * like fa_bwd's; FA_ERR_OUT_OF_MEMORY if it cannot be had.
  */
 int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int H, int Hkv, int N, int d, int causal,
