@@ -85,8 +85,6 @@ __device__ __forceinline__ int voff(int r, int col) {  // element offset of (r, 
 // (plus S_0 and softmax(S_0) up front). Group B (waves 4..7) runs one phase
 // behind group A (waves 0..3); each phase ends at a workgroup barrier, so on
 // every SIMD one wave's softmax runs while the other wave's products do.
-// Query rows are dealt in 32-row blocks alternating between the groups, so both
-// reach the causal diagonal on the same key tile.
 // QQ: the FP8 path's Q, quantised to E4M3 per 16 x 16 block (scale rule in
 // fa_common.h) and dequantised in registers as it is loaded (bf16 only).
 template <int D, bool CAUSAL, bool F16, bool QQ>
@@ -126,7 +124,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int grp = wave >> 2;                        // 0: group A, 1: group B
-  const int rblk = 2 * (wave & 3) + grp;            // this wave's 32-row block
+  // this wave's 32-row block: SIMD s (waves s and s + 4) holds blocks s and
+  // 7 - s, so on the tiles that cross the causal diagonal, where the lower
+  // blocks run out of keys, every SIMD keeps one wave busy and that wave's
+  // phases run without a partner on its SIMD (shorter than shared phases)
+  const int rblk = grp == 0 ? (wave & 3) : 7 - (wave & 3);
   const int tr_grp = lane >> 4, tr_i = lane & 15;   // transposing-read addressing
   const int tr_e = tr_i >> 2;
   const int wl = wave & 3;  // wave index within its group
