@@ -14,6 +14,12 @@ causal, and 2.5 times that for the backward. The printed JSON line carries:
              one launch sequence of three kernels and is timed as a unit
   roofline_fwd  the same for fa_fwd
   cpu_baseline  the CPU fp64 oracle on a bounded sample of the same workload
+
+`--all-workloads` instead times all five workloads of attn_inputs (the shapes
+of the "Performance Specifications" table of "RTX Flash Attention
+Implementation COMPLETE") in one run, forward and backward each, with the
+oracle timed on a bounded sample of distinct heads of each, and prints one
+JSON line per workload and causal mode (optionally a markdown table too).
 """
 from __future__ import annotations
 
@@ -113,32 +119,169 @@ def flops(w, causal):
     return f, 2.5 * f
 
 
-def cpu_baseline(w, causal, budget_s=15.0):
-    """The fp64 oracle (as it stands) on whole heads of the same workload."""
-    import numpy as np
-    import attn_inputs as ai
+def alg_bytes(w):
+    """The method's minimum HBM bytes per launch: the forward reads Q, K, V and
+    writes O (bf16) and the LSE (float32); the backward reads Q, K, V, O, dO
+    and writes dQ, dK, dV (bf16), and reads the LSE, writes and reads D."""
+    n = w.B * w.H * w.N
+    return 8.0 * n * w.d + 4.0 * n, 16.0 * n * w.d + 12.0 * n
+
+
+def host_cores():
+    return len(os.sched_getaffinity(0))
+
+
+def oracle_rate(w, causal, x, backward=True, budget_s=15.0, max_heads=64):
+    """The fp64 oracle, as it stands, on distinct whole heads (b, h) of the
+    workload's own inputs `x` (uint16 bits), in order (0, 0), (0, 1), ...,
+    until `budget_s` of oracle time; BLAS threads = the cores this process may
+    run on. FLOPs are counted like the GPU line (the oracle does the full N^2
+    work even when causal)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((int(i.get("num_threads", 1)) for i in threadpool_info()), default=1)
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_limits
+    cores = host_cores()
     f_fwd_head = 4.0 * w.N * w.N * w.d * (0.5 if causal else 1.0)
-    f_head = 3.5 * f_fwd_head
-    x = ai.make_qkv(1, 1, w.N, w.d, w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v, with_do=True)
-    heads, t_total = 0, 0.0
-    while t_total < budget_s and heads < 64:
-        q, k, v, do = (oracle.bf16_bits_to_f64(x[n][0, 0]) for n in ("q", "k", "v", "do"))
-        t0 = time.perf_counter()
-        oracle.head_forward(q, k, v, causal, w.scale)
-        oracle.head_backward(q, k, v, do, causal, w.scale)
-        t_total += time.perf_counter() - t0
-        heads += 1
-    return {"value": heads * f_head / t_total / 1e12, "unit": "TFLOP/s", "cores": cores,
+    f_head = f_fwd_head * (3.5 if backward else 1.0)
+    heads, t_total = [], 0.0
+    with threadpool_limits(limits=cores):
+        while t_total < budget_s and len(heads) < min(max_heads, w.B * w.H):
+            b, h = divmod(len(heads), w.H)
+            q, k, v = (oracle.bf16_bits_to_f64(x[n][b, h]) for n in ("q", "k", "v"))
+            t0 = time.perf_counter()
+            oracle.head_forward(q, k, v, causal, w.scale)
+            if backward:
+                oracle.head_backward(q, k, v, oracle.bf16_bits_to_f64(x["do"][b, h]), causal, w.scale)
+            t_total += time.perf_counter() - t0
+            heads.append((b, h))
+    what = "fwd+bwd" if backward else "fwd"
+    return {"value": len(heads) * f_head / t_total / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{heads} whole head(s) of {w.label} causal={causal}, fwd+bwd in fp64 "
-                      f"({t_total:.1f} s); FLOPs counted like the GPU line (the oracle does "
-                      f"the full N^2 work)"}
+            "sample": f"{len(heads)} distinct whole heads (b, h) = (0, 0) .. {heads[-1]} of "
+                      f"{w.label} causal={causal}, {what} in fp64, {t_total:.1f} s on {cores} "
+                      f"BLAS threads; FLOPs counted like the GPU line (the oracle does the full "
+                      f"N^2 work)",
+            "seconds": round(t_total, 2), "heads": len(heads)}
+
+
+def cpu_baseline(w, causal, x, budget_s=15.0):
+    """The oracle on a bounded sample of the timed workload (fwd + bwd)."""
+    r = oracle_rate(w, causal, x, backward=True, budget_s=budget_s)
+    r.pop("seconds")
+    r.pop("heads")
+    return r
+
+
+def device_inputs(w, dtype="bf16", hkv=None):
+    """Seeded inputs of workload w (with dO), as host bits and as device tensors."""
+    import numpy as np
+    import torch
+    import attn_inputs as ai
+    x = ai.make_qkv(w.B, w.H, w.N, w.d, w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v,
+                    with_do=True, dtype=dtype, Hkv=hkv or w.H)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    t = {n: torch.from_numpy(x[n].view(np.int16)).view(tdt).to("cuda:0") for n in x}
+    return x, t
+
+
+def time_launches(fa, w, t, causal, steps, warmup, backward=True):
+    """Per-launch HIP-event times (ms) of fa_fwd and fa_bwd over `steps` steps
+    (after `warmup` untimed ones), on the stream they are launched on, and the
+    wall time per step."""
+    import numpy as np
+    import torch
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(q.device)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.forward(q, k, v, causal, w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if backward:
+            fa.backward(do, q, k, v, o, lse, causal, w.scale, dq=dq, dk=dk, dv=dv)
+            if ev is not None:
+                ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if backward else [0.0]
+    return fwd_ms, bwd_ms, wall * 1e3 / steps, (o, lse)
+
+
+def all_workloads(args):
+    """One JSON line per workload and causal mode: fa_fwd and fa_bwd times,
+    TFLOP/s, % of the bf16 peak, algorithmic HBM GB/s, and the oracle's rate on
+    a bounded sample of the same inputs."""
+    import numpy as np
+    import torch
+    import attn_inputs as ai
+    import exact_tiled_attention_17_amd as fa
+    torch.cuda.set_device(0)
+    rows = []
+    for wname in ("c1", "c2", "c3", "c4", "c5"):
+        w = ai.WORKLOADS[wname]
+        x, t = device_inputs(w)
+        for causal in w.causal_modes:
+            fwd_ms, bwd_ms, step_ms, _ = time_launches(fa, w, t, causal, args.steps, args.warmup)
+            f_fwd, f_bwd = flops(w, causal)
+            b_fwd, b_bwd = alg_bytes(w)
+            tf, tb = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+            r = {"workload": wname, "shape": w.label, "causal": causal,
+                 "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4), "step_ms": round(tf + tb, 4),
+                 "fwd_ms_stats": time_stats(fwd_ms), "bwd_ms_stats": time_stats(bwd_ms),
+                 "fwd_tflops": round(f_fwd / tf / 1e9, 1),
+                 "bwd_tflops": round(f_bwd / tb / 1e9, 1),
+                 "step_tflops": round((f_fwd + f_bwd) / (tf + tb) / 1e9, 1),
+                 "fwd_pct_peak": round(100 * f_fwd / tf / 1e9 / PEAK_BF16_TFLOPS, 2),
+                 "step_pct_peak": round(100 * (f_fwd + f_bwd) / (tf + tb) / 1e9 / PEAK_BF16_TFLOPS, 2),
+                 "fwd_alg_hbm_gbs": round(b_fwd / tf / 1e6, 1),
+                 "bwd_alg_hbm_gbs": round(b_bwd / tb / 1e6, 1),
+                 "page_context_ms": PAGE_TIMES_MS.get(w.label)}
+            if not args.no_cpu_baseline:
+                budget = 6.0
+                r["oracle_fwd"] = oracle_rate(w, causal, x, backward=False, budget_s=budget)
+                r["oracle_fwd_bwd"] = oracle_rate(w, causal, x, backward=True, budget_s=budget)
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+        del x, t
+        torch.cuda.empty_cache()
+    if args.report_md:
+        with open(args.report_md, "w") as f:
+            f.write(workload_table(rows, args))
+    return rows
+
+
+def workload_table(rows, args):
+    """Markdown table of all_workloads' rows."""
+    out = ["| workload | B×H×N×d | causal | fa_fwd ms | fwd TFLOP/s (% peak) | fa_bwd ms | "
+           "step TFLOP/s (% peak) | fwd / bwd alg. HBM GB/s | oracle fwd / fwd+bwd GFLOP/s "
+           "(heads, cores) | page ms |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        orc = "—"
+        if "oracle_fwd" in r:
+            a, b = r["oracle_fwd"], r["oracle_fwd_bwd"]
+            orc = (f"{a['value'] * 1e3:.1f} ({a['heads']}) / {b['value'] * 1e3:.1f} ({b['heads']}), "
+                   f"{a['cores']} cores")
+        out.append(f"| {r['workload']} | {r['shape']} | {r['causal']} | {r['fwd_ms']:.4f} | "
+                   f"{r['fwd_tflops']:.0f} ({r['fwd_pct_peak']:.1f}%) | {r['bwd_ms']:.4f} | "
+                   f"{r['step_tflops']:.0f} ({r['step_pct_peak']:.1f}%) | "
+                   f"{r['fwd_alg_hbm_gbs']:.0f} / {r['bwd_alg_hbm_gbs']:.0f} | {orc} | "
+                   f"{r['page_context_ms']} |")
+    return "\n".join(out) + "\n"
 
 
 def main():
@@ -156,12 +299,19 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warmup, run one device-to-device copy of this many MiB "
                          "(a known-size kernel to calibrate HBM byte counters against)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="time all five workloads (one JSON line each) instead of the step line")
+    ap.add_argument("--report-md", default="", help="with --all-workloads: also write a markdown table")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
               "is independent, so N GPUs would each run this same kernel on B*H/N heads.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.all_workloads:
+        all_workloads(args)
+        return
 
     import numpy as np
     import torch
@@ -177,15 +327,10 @@ def main():
     default_launch = hkv == w.H and args.dtype == "bf16"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = ai.make_qkv(w.B, w.H, w.N, w.d, w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v,
-                    with_do=True, dtype=args.dtype, Hkv=hkv)
-    tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
-    t = {n: torch.from_numpy(x[n].view(np.int16)).view(tdt).to(dev) for n in x}
-    del x
+    x, t = device_inputs(w, args.dtype, hkv)
+    if not default_launch or args.no_cpu_baseline:
+        del x  # the host bits serve only the CPU baseline
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stream = torch.cuda.current_stream(dev)
     if args.copy_probe_mib > 0:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -195,27 +340,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        fa.forward(q, k, v, causal, w.scale, out=o, lse=lse)
-        if ev is not None:
-            ev[1].record(stream)
-        if not args.fwd_only:
-            fa.backward(do, q, k, v, o, lse, causal, w.scale, dq=dq, dk=dk, dv=dv)
-            if ev is not None:
-                ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    fwd_ms, bwd_ms, ms_step, (o, lse) = time_launches(fa, w, t, causal, args.steps, args.warmup,
+                                                      backward=not args.fwd_only)
 
     # the per-key attention mass (a second pass after the forward, not part of
     # the training step): timed on its own, same stream, same inputs
@@ -247,10 +373,7 @@ def main():
         fp8_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
         del o8, l8
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if not args.fwd_only else [0.0]
     f_fwd, f_bwd = flops(w, causal)
-    ms_step = wall * 1e3 / args.steps
     t_fwd = float(np.mean(fwd_ms))
     t_bwd = float(np.mean(bwd_ms))
     fwd_tf = f_fwd / (t_fwd * 1e-3) / 1e12
@@ -328,7 +451,7 @@ def main():
     if args.dtype != "bf16":
         out["config"]["workload"] += f", {args.dtype} inputs"
     if not args.no_cpu_baseline and default_launch:
-        out["cpu_baseline"] = cpu_baseline(w, causal)
+        out["cpu_baseline"] = cpu_baseline(w, causal, x)
     print(json.dumps(out), flush=True)
 
 

@@ -29,8 +29,9 @@
 // float32 atomics cost more than recomputing S and dP in a second pass, so
 // this backward recomputes instead.
 //
-// Global reads go through buffer resources, so rows past the end of the
-// sequence read as zeros without branches.
+// Global reads go through buffer resources whose range check ends at row N,
+// so rows past the end of the sequence read as zeros without branches (the
+// rule is at make_rsrc in fa_common.h).
 
 #include <type_traits>
 
@@ -166,27 +167,29 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     return p;
   };
+  // Each step's tiles are read through resources that start at its first
+  // query and end at query N, so the rows of a ragged last step and every row
+  // of a padding step (all past N) read as zeros and touch no memory.
   auto load_step = [&](Step p, __bf16* qd, __bf16* od, float* rsd) __attribute__((always_inline)) {
     const size_t qh = (size_t)(qh0 + p.g);  // query head
     const size_t head = qh * (size_t)N * D;
-    const auto rQ = make_rsrc(Q + head, head_bytes);
-    const auto rdO = make_rsrc(dO + head, head_bytes);
-    // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
-    const auto rL2 = make_rsrc(rowstat + qh * N, (uint32_t)N * 4u);
-    const auto rDD = make_rsrc(rowstat + (size_t)BH * N + qh * N, (uint32_t)N * 4u);
     const int q0 = (i0 + p.t) * BRB;
-    const uint32_t row0 = (uint32_t)q0 * (D * 2);
+    const auto rQ = rows_rsrc(Q + head, q0, N, D * 2);
+    const auto rdO = rows_rsrc(dO + head, q0, N, D * 2);
+    // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
+    const auto rL2 = rows_rsrc(rowstat + qh * N, q0, N, 4);
+    const auto rDD = rows_rsrc(rowstat + (size_t)BH * N + qh * N, q0, N, 4);
 #pragma unroll
     for (int m = 0; m < LM; ++m) {
       const int n = wave + 8 * m;
       if (n < TI) {
-        buf_load16_lds(rQ, src_w[m], row0, qd + 64 * n * 8);
-        buf_load16_lds(rdO, src_w[m], row0, od + 64 * n * 8);
+        buf_load16_lds(rQ, src_w[m], qd + 64 * n * 8);
+        buf_load16_lds(rdO, src_w[m], od + 64 * n * 8);
       }
     }
     if (wave == 0) {
-      buf_load4_lds(rL2, 4u * lane, (uint32_t)q0 * 4u, rsd);
-      buf_load4_lds(rDD, 4u * lane, (uint32_t)q0 * 4u, rsd + BRB);
+      buf_load4_lds(rL2, 4u * lane, rsd);
+      buf_load4_lds(rDD, 4u * lane, rsd + BRB);
     }
   };
 
@@ -505,8 +508,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rQ = make_rsrc(Q + head, head_bytes);
-  const auto rK = make_rsrc(K + kvhead, head_bytes);
-  const auto rV = make_rsrc(V + kvhead, head_bytes);
+  const __bf16* const Kh = K + kvhead;
+  const __bf16* const Vh = V + kvhead;
   const auto rdO = make_rsrc(dO + head, head_bytes);
   const auto rO = make_rsrc(O + head, head_bytes);
   const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
@@ -559,14 +562,16 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   uint32_t src_b[LM];  // this wave's offsets as one of the four in-loop loaders
 #pragma unroll
   for (int m = 0; m < LM; ++m) src_b[m] = src(wl + 4 * m);
-  auto load_tile = [&](auto NL, __amdgpu_buffer_rsrc_t rsrc, int w, int j, __bf16* t)
+  // tile j of K or V (src = the head's first row), through a resource that
+  // starts at the tile's first key and ends at key N
+  auto load_tile = [&](auto NL, const __bf16* src_head, int w, int j, __bf16* t)
       __attribute__((always_inline)) {
     constexpr int nl = decltype(NL)::value;
-    const uint32_t row0 = (uint32_t)j * (BC * D * 2);
+    const auto r = rows_rsrc(src_head, j * BC, N, D * 2);
 #pragma unroll
     for (int m = 0; m * nl < TI; ++m) {
       const int n = m * nl + w;
-      if (n < TI) buf_load16_lds(rsrc, nl == 4 ? src_b[m] : src(n), row0, t + 64 * n * 8);
+      if (n < TI) buf_load16_lds(r, nl == 4 ? src_b[m] : src(n), t + 64 * n * 8);
     }
   };
   using four = std::integral_constant<int, 4>;
@@ -698,14 +703,15 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // Every wave runs T4 = T rounded up to 4 tiles (the barriers must match):
   // the full work, in groups of 4, up to its last needed tile rounded up to 4
   // (the extra tiles are fully masked, so they add nothing), then only the
-  // loads and barriers. All T4 tiles are loaded (past the sequence end they
-  // read as zeros), so no product ever reads a buffer that was never filled.
+  // loads and barriers. All T4 tiles are loaded, so no product ever reads a
+  // buffer that was never filled: a tile past the sequence end gets an empty
+  // resource (rows_rsrc) and fills its buffer with zeros without reading memory.
   const int T4 = (T + 3) & ~3;
   const int jw4 = (jw_last + 4) & ~3;
-  load_tile(eight{}, rK, wave, 0, ks0);
-  load_tile(eight{}, rV, wave, 0, vs0);
-  load_tile(eight{}, rK, wave, 1, ks1);
-  load_tile(eight{}, rV, wave, 1, vs1);
+  load_tile(eight{}, Kh, wave, 0, ks0);
+  load_tile(eight{}, Vh, wave, 0, vs0);
+  load_tile(eight{}, Kh, wave, 1, ks1);
+  load_tile(eight{}, Vh, wave, 1, vs1);
   wait_vmem_all();
   __syncthreads();
   if (grp == 1) __syncthreads();
@@ -717,8 +723,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __bf16* const kbuf[4] = {ks0, ks1, ks2, ks3};
     __bf16* const vbuf[2] = {vs0, vs1};
     if (grp == 1 && t + 2 < T4) {
-      load_tile(four{}, rK, wl, t + 2, kbuf[(p + 2) & 3]);
-      load_tile(four{}, rV, wl, t + 2, vbuf[p & 1]);
+      load_tile(four{}, Kh, wl, t + 2, kbuf[(p + 2) & 3]);
+      load_tile(four{}, Vh, wl, t + 2, vbuf[p & 1]);
     }
     vphase(t);
     slot_barrier();
@@ -740,8 +746,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (; t < T4; ++t) {
     if (grp == 1 && t + 2 < T4) {
       __bf16* kf = ((t + 2) & 3) == 0 ? ks0 : ((t + 2) & 3) == 1 ? ks1 : ((t + 2) & 3) == 2 ? ks2 : ks3;
-      load_tile(four{}, rK, wl, t + 2, kf);
-      load_tile(four{}, rV, wl, t + 2, (t & 1) ? vs1 : vs0);
+      load_tile(four{}, Kh, wl, t + 2, kf);
+      load_tile(four{}, Vh, wl, t + 2, (t & 1) ? vs1 : vs0);
     }
     slot_barrier();
     wait_vmem_all();

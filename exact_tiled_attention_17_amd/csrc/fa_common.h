@@ -142,12 +142,31 @@ __device__ __forceinline__ uint16_t to16(float v) {
   else return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride):
-// loads at byte offsets at or past `bytes` return zeros instead of faulting,
-// which is how the kernels read ragged tails without branches.
+// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride).
+// The range check of a raw buffer access (CDNA3 / CDNA4 ISA reference guides,
+// buffer addressing, range checking) compares the instruction's immediate
+// offset plus its per-lane offset with the record count; the scalar offset
+// is not part of it. A load whose immediate + per-lane offset is at or past
+// `bytes` returns zeros (into registers or LDS) and touches no memory. The
+// kernels therefore never put a row offset in the scalar operand: each tile
+// gets a resource of its own (rows_rsrc), and only offsets inside the tile
+// go in the per-lane operand.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
+}
+
+// Resource over rows row0 .. nrows - 1 of an array of `row_bytes`-byte rows at
+// `base` (wave-uniform arguments, so it lives in scalar registers): per-lane
+// offset o reads byte o of row row0, and offsets that reach row nrows or
+// beyond read as zeros. A tile that starts at or past nrows gets an empty
+// resource at `base` itself, so no address past the array is ever formed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int row0, int nrows,
+                                                            uint32_t row_bytes) {
+  const bool inside = row0 < nrows;
+  const char* p = static_cast<const char*>(base) + (inside ? (size_t)row0 * row_bytes : 0);
+  const uint32_t bytes = inside ? (uint32_t)(nrows - row0) * row_bytes : 0u;
+  return make_rsrc(p, bytes);
 }
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
@@ -155,20 +174,18 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
 // lds_base + 16 l (lds_base is wave-uniform); the source is byte voff (per
-// lane) + soff (wave-uniform) of the buffer. Completion is tracked by vmcnt,
-// like any vector-memory load.
-__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                               __bf16* lds_base) {
+// lane, range-checked) of the buffer. Completion is tracked by vmcnt, like
+// any vector-memory load. The scalar offset is always 0 (see make_rsrc).
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, __bf16* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voff, soff, 0, 0);
+                                           voff, 0, 0, 0);
 }
 
 // 4 bytes per lane from a buffer straight into LDS: lane l's bytes land at
 // lds_base + 4 l.
-__device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                              void* lds_base) {
+__device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
-                                           voff, soff, 0, 0);
+                                           voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {

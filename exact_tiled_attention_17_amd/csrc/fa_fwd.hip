@@ -38,8 +38,9 @@
 //    nothing. The reference max
 //    only moves when the row max outgrows it by 2^15, so the O^T rescale runs on
 //    few tiles.
-//  * Global reads go through buffer resources: rows past the end of the
-//    sequence read as zeros, with no branches around the loads.
+//  * Global reads go through buffer resources whose range check ends at row
+//    N: rows past the end of the sequence read as zeros, with no branches
+//    around the loads (make_rsrc in fa_common.h gives the rule).
 
 #include <type_traits>
 
@@ -138,8 +139,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rQ = make_rsrc(Q + head, head_bytes);
-  const auto rK = make_rsrc(K + kvhead, head_bytes);
-  const auto rV = make_rsrc(V + kvhead, head_bytes);
+  const __bf16* const Kh = K + kvhead;
+  const __bf16* const Vh = V + kvhead;
 
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * rblk;  // first query row of this wave
@@ -190,9 +191,9 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // the 64 consecutive 16-byte chunk positions [64 n, 64 n + 64) of the tile's
   // LDS image, each lane fetching the global chunk that the layout puts at its
   // position. The instructions of a tile are dealt round-robin over NL loader
-  // waves (w = index among them). Source offsets are split into a per-lane part
-  // (below, relative to the tile's first row) and the tile's row offset, which
-  // goes in the scalar offset.
+  // waves (w = index among them). Each tile is read through a resource that
+  // starts at its first row and ends at row N (rows_rsrc), with per-lane
+  // offsets relative to the tile's first row: rows past N read as zeros.
   auto k_src = [&](int n) -> uint32_t {  // padding positions fetch chunk 0 again
     const int i = 64 * n + lane;
     const int kr = i / KCH, pos = i % KCH;
@@ -201,29 +202,31 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // V: 64 positions are whole rows (64 / CH of them, a multiple of the swizzle
   // period), so instruction n's offsets are instruction 0's plus 1024 n bytes.
   const uint32_t v_src0 = (uint32_t)((lane / CH) * (D * 2) + (((lane % CH) ^ vswz<D>(lane / CH)) * 16));
-  // this wave's K offsets as one of the four in-loop loaders (n = wl + 4 m)
+  // this wave's K and V offsets as one of the four in-loop loaders (n = wl + 4 m)
   constexpr int KM = (C::K_INSTR + 3) / 4;
-  uint32_t k_src_b[KM];
+  constexpr int VM = (C::V_INSTR + 3) / 4;
+  uint32_t k_src_b[KM], v_src_b[VM];
 #pragma unroll
   for (int m = 0; m < KM; ++m) k_src_b[m] = k_src(wl + 4 * m);
+#pragma unroll
+  for (int m = 0; m < VM; ++m) v_src_b[m] = v_src0 + 1024u * (wl + 4 * m);
 
   auto load_k = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
     constexpr int nl = decltype(NL)::value;
-    const uint32_t row0 = (uint32_t)j * (BC * D * 2);
+    const auto r = rows_rsrc(Kh, j * BC, N, D * 2);
 #pragma unroll
     for (int m = 0; m * nl < C::K_INSTR; ++m) {
       const int n = m * nl + w;
-      if (n < C::K_INSTR)
-        buf_load16_lds(rK, nl == 4 ? k_src_b[m] : k_src(n), row0, t + 64 * n * 8);
+      if (n < C::K_INSTR) buf_load16_lds(r, nl == 4 ? k_src_b[m] : k_src(n), t + 64 * n * 8);
     }
   };
   auto load_v = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
     constexpr int nl = decltype(NL)::value;
-    const uint32_t row0 = (uint32_t)j * (BC * D * 2);
+    const auto r = rows_rsrc(Vh, j * BC, N, D * 2);
 #pragma unroll
     for (int m = 0; m * nl < C::V_INSTR; ++m) {
       const int n = m * nl + w;
-      if (n < C::V_INSTR) buf_load16_lds(rV, v_src0, row0 + 1024u * n, t + 64 * n * 8);
+      if (n < C::V_INSTR) buf_load16_lds(r, nl == 4 ? v_src_b[m] : v_src0 + 1024u * n, t + 64 * n * 8);
     }
   };
   using four = std::integral_constant<int, 4>;

@@ -59,9 +59,9 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int hh = lane >> 5;
 
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto rQ = make_rsrc(Q + (size_t)bh * N * D, head_bytes);
+  const __bf16* const Qh = Q + (size_t)bh * N * D;
+  const float* const Lh = LSE + (size_t)bh * N;
   const auto rK = make_rsrc(K + (size_t)(bh / G) * N * D, head_bytes);
-  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int k0 = kb * C::BCB;
   const int kw0 = k0 + 32 * wave;  // this wave's first key
@@ -74,7 +74,9 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // ---- step loads, straight from HBM into LDS: instruction n fills chunk
   // positions [64 n, 64 n + 64) of the Q tile (dealt round-robin over the
-  // waves); wave 0 also loads the 64 LSE values ------------------------------
+  // waves); wave 0 also loads the 64 LSE values. Both go through resources
+  // that start at the step's first query and end at query N, so the rows past
+  // N of a ragged last step read as zeros --------------------------------------
   uint32_t src_w[LM];
 #pragma unroll
   for (int m = 0; m < LM; ++m) {
@@ -87,10 +89,10 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int nsteps = nqt - i0;
   auto load_step = [&](int s, __bf16* qd, float* ld) __attribute__((always_inline)) {
     const int q0 = (i0 + s) * BRB;
+    const auto rQ = rows_rsrc(Qh, q0, N, D * 2);
 #pragma unroll
-    for (int m = 0; m < LM; ++m)
-      buf_load16_lds(rQ, src_w[m], (uint32_t)q0 * (D * 2), qd + 64 * (wave + C::NW * m) * 8);
-    if (wave == 0) buf_load4_lds(rL, 4u * lane, (uint32_t)q0 * 4u, ld);
+    for (int m = 0; m < LM; ++m) buf_load16_lds(rQ, src_w[m], qd + 64 * (wave + C::NW * m) * 8);
+    if (wave == 0) buf_load4_lds(rows_rsrc(Lh, q0, N, 4), 4u * lane, ld);
   };
 
   int rw = tile_off<D>(l32, 8 * hh);  // operand row l32, chunk hh; k-step st at rw ^ 16 st
