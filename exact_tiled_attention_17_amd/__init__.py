@@ -1,8 +1,8 @@
 """Exact tiled attention for AMD Instinct MI355X (gfx950).
 
 A thin binding of ``libfa.so`` (C ABI in ``include/fa.h``). The functions
-``fa_fwd``, ``fa_bwd``, ``fa_fwd_ex``, ``fa_bwd_ex``, ``fa_key_mass``,
-``fa_quantize_e4m3``, ``fa_fwd_fp8`` and ``fa_status_string`` mirror the C
+``fa_fwd``, ``fa_bwd``, ``fa_fwd_ex``, ``fa_bwd_ex``, ``fa_bwd_noalloc``,
+``fa_key_mass``, ``fa_quantize_e4m3``, ``fa_fwd_fp8`` and ``fa_status_string`` mirror the C
 entry points one to one (raw device pointers as Python ints, ``stream`` as a
 hipStream_t handle). ``forward``, ``backward``, ``key_mass``,
 ``quantize_e4m3`` and ``forward_fp8`` are conveniences over torch tensors:
@@ -21,7 +21,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_key_mass", "fa_quantize_e4m3",
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_noalloc", "fa_key_mass",
+           "fa_quantize_e4m3", "FA_NOALLOC_MAX_ROWS",
            "fa_fwd_fp8", "fa_status_string", "fa_last_hip_error",
            "forward", "backward", "key_mass", "quantize_e4m3", "forward_fp8", "load", "FAError", "LIB_PATH", "FA_DTYPE_BF16", "FA_DTYPE_F16"]
 
@@ -32,6 +33,9 @@ FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 FA_ERR_OUT_OF_MEMORY = 4
+FA_ERR_TOO_LARGE = 5
+
+FA_NOALLOC_MAX_ROWS = 2097152  # query rows (B * H * N) of fa_bwd_noalloc's static workspace
 
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
@@ -75,6 +79,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci,
                               vp]
     lib.fa_bwd_ex.restype = ci
+    lib.fa_bwd_noalloc.argtypes = lib.fa_bwd_ex.argtypes
+    lib.fa_bwd_noalloc.restype = ci
     lib.fa_key_mass.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     lib.fa_key_mass.restype = ci
     lib.fa_quantize_e4m3.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
@@ -120,6 +126,14 @@ def fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, causal, softmax_
     """C ``fa_bwd_ex``: as ``fa_bwd`` with Hkv K/V heads and the element type (FA_DTYPE_*)."""
     return load().fa_bwd_ex(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, int(causal),
                             float(softmax_scale), int(dtype), stream or None)
+
+
+def fa_bwd_noalloc(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, causal, softmax_scale,
+                   dtype, stream) -> int:
+    """C ``fa_bwd_noalloc``: ``fa_bwd_ex`` with its scratch in the library's static per-device
+    workspace (no allocation; B * H * N <= FA_NOALLOC_MAX_ROWS); returns the status."""
+    return load().fa_bwd_noalloc(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Hkv, N, d, int(causal),
+                                 float(softmax_scale), int(dtype), stream or None)
 
 
 def fa_key_mass(Q, K, LSE, mass, B, H, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:

@@ -5,13 +5,44 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
+// fa_bwd_noalloc's workspace: the backward's two float32 planes of row
+// statistics for up to FA_NOALLOC_MAX_ROWS query rows (16 MiB), one copy in
+// the memory of each GPU the library runs on, kept until the process ends.
+// In host code `scratch` is only a host-side stand-in: kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[2 * (size_t)FA_NOALLOC_MAX_ROWS];
+
 namespace {
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
+
+// Device address of `scratch` on each device, looked up on the first
+// fa_bwd_noalloc call made with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int hip_status(hipError_t e, int status_on_error) {
   if (e == hipSuccess) return FA_OK;
@@ -82,6 +113,26 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const 
   const hipError_t e = fa::launch_bwd(a);
   const hipError_t f = hipFreeAsync(scratch, s);
   return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
+}
+
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                   const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                   int d, int causal, float softmax_scale, int dtype, void* stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
+  int st = check_common(B, H, Hkv, N, d, causal, softmax_scale);
+  if (st != FA_OK) return st;
+  for (const void* p : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
+    if ((st = check_tensor(p)) != FA_OK) return st;
+  if (LSE == nullptr || !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N > FA_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+
+  float* ws = nullptr;
+  const hipError_t w = scratch_on_current_device(&ws);
+  if (w != hipSuccess) return hip_status(w, FA_ERR_HIP);
+  fa::BwdArgs a{Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, d, causal != 0, softmax_scale,
+                reinterpret_cast<hipStream_t>(stream), ws, dtype == FA_DTYPE_F16, Hkv};
+  a.no_split = true;
+  return hip_status(fa::launch_bwd(a), FA_ERR_HIP);
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
@@ -166,6 +217,9 @@ const char* fa_status_string(int status) {
       return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128, element type bf16 or f16";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call or kernel launch failed";
     case FA_ERR_OUT_OF_MEMORY: return "FA_ERR_OUT_OF_MEMORY: scratch allocation failed";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: B * H * N exceeds the static workspace of fa_bwd_noalloc "
+             "(FA_NOALLOC_MAX_ROWS = 2097152 query rows)";
     default: return "unknown fa_status";
   }
 }

@@ -789,7 +789,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   {
     const int nkb = (a.N + C::BCB - 1) / C::BCB;
     const int G = a.H / a.Hkv;
-    const int S = dkdv_splits(a.B, a.H, a.Hkv, a.N, a.d);
+    const int S = a.no_split ? 1 : dkdv_splits(a.B, a.H, a.Hkv, a.N, a.d);
     float* part = S > 1 ? a.rowstat + rowstat_floats(a.B, a.H, a.N) : nullptr;
     const long long total = (long long)nkb * a.B * a.Hkv * S;
     const hipError_t e = launch_kernel(

@@ -40,6 +40,7 @@ struct BwdArgs {
                   // every row, then D = dO . O), then the dK/dV partial sums if split
   bool f16;       // element type of the 16-bit tensors: IEEE binary16 (true) or bf16
   int Hkv;        // K/V heads (K, V, dK, dV are [B,Hkv,N,d]); divides H
+  bool no_split = false;  // never split the dK/dV work (scratch holds the row statistics only)
 };
 
 struct MassArgs {

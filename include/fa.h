@@ -52,9 +52,10 @@
  * kernel launch failed at enqueue time; faults inside a kernel surface at the
  * caller's next synchronisation. Calls only enqueue work on `stream` (a
  * hipStream_t; NULL is the default stream) and return; results are valid once
- * the stream has reached them. The library holds no global mutable state (only
- * a per-thread record of the last HIP error), so calls from several threads on
- * different streams are safe.
+ * the stream has reached them. Apart from fa_bwd_noalloc's per-device
+ * workspace, the library holds no global mutable state (only a per-thread
+ * record of the last HIP error), so calls from several threads on different
+ * streams are safe.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -68,7 +69,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad shape, bad scale or flag */
   FA_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128, or unknown fa_dtype */
   FA_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
-  FA_ERR_OUT_OF_MEMORY = 4  /* fa_bwd, fa_key_mass or fa_fwd_fp8 could not get its scratch */
+  FA_ERR_OUT_OF_MEMORY = 4, /* fa_bwd, fa_key_mass or fa_fwd_fp8 could not get its scratch */
+  FA_ERR_TOO_LARGE = 5      /* fa_bwd_noalloc: B * H * N exceeds FA_NOALLOC_MAX_ROWS */
 } fa_status;
 
 /*
@@ -162,6 +164,37 @@ int fa_bwd_ex(const void* Q, const void* K, const void* V, const void* O,
               const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
               int B, int H, int Hkv, int N, int d, int causal,
               float softmax_scale, int dtype, void* stream);
+
+/* Query rows (B * H * N) that fa_bwd_noalloc's static workspace holds. */
+#define FA_NOALLOC_MAX_ROWS 2097152
+
+/*
+ * fa_bwd_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, layout, results and validation as fa_bwd_ex; it calls no
+ * allocating routine.
+ *
+ * The backward's scratch (two float32 planes of row statistics, 8 bytes per
+ * query row) lives in a workspace the library keeps in device memory of each
+ * GPU it runs on: 8 * FA_NOALLOC_MAX_ROWS bytes = 16 MiB, held until the
+ * process ends; its address is looked up on the first call on each device.
+ * B * H * N must not exceed FA_NOALLOC_MAX_ROWS (FA_ERR_TOO_LARGE otherwise;
+ * 4 x 64 x 4096 is 2^20 rows). Nothing in it needs clearing: every row the
+ * call reads is written earlier in the same call. The dK/dV work is never
+ * split over the query heads of a K/V head (no partial sums), so with few K/V
+ * heads (B * Hkv * ceil(N / 128) < 1024) it runs on fewer workgroups than
+ * fa_bwd_ex and sums dK, dV in another order; otherwise its results are
+ * bitwise those of fa_bwd_ex.
+ *
+ * Every call on one GPU shares that GPU's workspace: calls that overlap in
+ * time on one GPU (on two streams, or from two threads) race and give wrong
+ * results; order them on one stream. FA_ERR_HIP if the workspace's device
+ * address cannot be obtained.
+ */
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                   const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+                   int B, int H, int Hkv, int N, int d, int causal,
+                   float softmax_scale, int dtype, void* stream);
 
 /*
  * Attention mass per key position ("GPU Performance Optimization Batch 1 -

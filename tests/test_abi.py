@@ -24,9 +24,9 @@ def header_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_fwd_fp8",
-                                  "fa_key_mass", "fa_last_hip_error", "fa_quantize_e4m3",
-                                  "fa_status_string"]
+    assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_ex",
+                                  "fa_fwd_fp8", "fa_key_mass", "fa_last_hip_error",
+                                  "fa_quantize_e4m3", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,8 +38,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert fa.fa_status_string(fa.FA_OK).startswith("FA_OK")
-    for st in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, fa.FA_ERR_OUT_OF_MEMORY):
+    for st in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, fa.FA_ERR_OUT_OF_MEMORY,
+               fa.FA_ERR_TOO_LARGE):
         assert fa.fa_status_string(st).startswith("FA_ERR")
+    assert str(fa.FA_NOALLOC_MAX_ROWS) in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
     assert fa.fa_status_string(12345) == "unknown fa_status"
     assert fa.fa_last_hip_error() == "hipSuccess"
 
@@ -234,3 +236,29 @@ def test_torch_fp8_wrappers_check_before_calling():
         fa.forward_fp8(q, q, q)
     with pytest.raises(TypeError):
         fa.quantize_e4m3(q.float())
+
+
+@pytest.mark.parametrize("dtype", [fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16])
+def test_noalloc_validates_like_bwd_ex(dtype):
+    """fa_bwd_noalloc rejects what fa_bwd_ex rejects, before any HIP call."""
+    def call(B=1, H=2, Hkv=2, N=16, d=128, causal=0, scale=0.125, LSE=P, dt=dtype, Q=P):
+        return fa.fa_bwd_noalloc(Q, P, P, P, LSE, P, P, P, P, B, H, Hkv, N, d, causal, scale, dt, None)
+    assert call(dt=7) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(B=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Hkv=3) == fa.FA_ERR_INVALID_ARG
+    assert call(causal=2) == fa.FA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert call(LSE=None) == fa.FA_ERR_INVALID_ARG
+    assert call(Q=P + 8) == fa.FA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_problems_beyond_its_workspace():
+    """B * H * N above FA_NOALLOC_MAX_ROWS is FA_ERR_TOO_LARGE, decided on the host."""
+    M = fa.FA_NOALLOC_MAX_ROWS
+    assert M == 2 ** 21
+    # one row over: 1 x 1 x (M + 1) with d = 64 (N * d < 2^31)
+    assert fa.fa_bwd_noalloc(P, P, P, P, P, P, P, P, P, 1, 1, 1, M + 1, 64, 1, 0.125,
+                             fa.FA_DTYPE_BF16, None) == fa.FA_ERR_TOO_LARGE
+    assert fa.fa_bwd_noalloc(P, P, P, P, P, P, P, P, P, 8, 64, 8, 4097, 128, 1, 0.125,
+                             fa.FA_DTYPE_BF16, None) == fa.FA_ERR_TOO_LARGE
