@@ -8,8 +8,8 @@
 //     tiles like the forward (and with its two-group schedule): S and dP are
 //     recomputed and dQ += dS K is summed in registers, so dQ needs no atomics
 //     and no float32 scratch. It first forms its rows' statistics, D_i =
-//     dO_i . O_i (float32) and the LSE in base 2, and stores them as two
-//     planes for the next pass.
+//     dO_i . O_i (float32) and the LSE in base 2, and stores them (the LSE in
+//     base 2 and -D) as two planes for the next pass.
 //  2. bwd_dkdv_kernel: one workgroup per (batch, head, block of 128 keys); each
 //     32-key block has a P-wave (dV) and a dS-wave (dK) on one SIMD, holding
 //     float32 accumulators for the whole sweep over query tiles of 64 rows,
@@ -17,7 +17,8 @@
 //     operands that need them transposed use gfx950's transposing LDS read
 //     instead of a second, transposed copy. Per query tile, on 32x32x16 bf16
 //     matrix cores:
-//        S = Q K^T, dP = dO V^T        (lane = one key, 16 queries)
+//        S = Q K^T, dP - D = dO V^T - D (lane = one key, 16 queries; the
+//                                       accumulator starts at -D)
 //        P = exp2(c S - LSE2), dS = P (dP - D)
 //        dV += P^T dO, dK += dS^T Q    (P^T, dS^T straight from registers)
 //     Causal: query tiles that see none of the block's keys are skipped.
@@ -96,7 +97,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) u32x4 ps0[C::KBLK][2 * QB][64];  // P^T operands, lane-major
   __shared__ __attribute__((aligned(16))) u32x4 ps1[C::KBLK][2 * QB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ps2[C::KBLK][2 * QB][64];
-  __shared__ __attribute__((aligned(16))) float rs0[2 * BRB];  // LSE2 of the step's queries, then D
+  __shared__ __attribute__((aligned(16))) float rs0[2 * BRB];  // LSE2 of the step's queries, then -D
   __shared__ __attribute__((aligned(16))) float rs1[2 * BRB];
   __shared__ __attribute__((aligned(16))) float rs2[2 * BRB];
 
@@ -176,7 +177,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int q0 = (i0 + p.t) * BRB;
     const auto rQ = rows_rsrc(Q + head, q0, N, D * 2);
     const auto rdO = rows_rsrc(dO + head, q0, N, D * 2);
-    // row statistics: LSE in base 2 for all rows, then D = dO . O for all rows
+    // row statistics: LSE in base 2 for all rows, then -D = -dO . O for all rows
     const auto rL2 = rows_rsrc(rowstat + qh * N, q0, N, 4);
     const auto rDD = rows_rsrc(rowstat + (size_t)BH * N + qh * N, q0, N, 4);
 #pragma unroll
@@ -208,15 +209,29 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   f32x16 sd[QB];      // S (P-wave) or dP (dS-wave) of a step: lane = one key, 16 queries
   u32x4 opnd[QB][2];  // P^T (P-wave) or dS^T (dS-wave) as A operands, 2 k-steps each
 
-  // sd = (Q or dO tile rows) x frag^T, one product per 32-query block. In both
-  // products the operand reads run R products ahead of their use, fenced so
-  // that the scheduler keeps that depth.
+  // sd = (Q or dO tile rows) x frag^T, one product per 32-query block,
+  // accumulated onto zeros (S) or onto -D of each query (dP - D: `negd`, the
+  // step's -D plane in LDS), so that dS needs no subtraction. In both products
+  // the operand reads run R products ahead of their use, fenced so that the
+  // scheduler keeps that depth.
   constexpr int R = 2;
-  auto first_product = [&](const __bf16* tile) __attribute__((always_inline)) {
+  auto first_product = [&](const __bf16* tile, const float* negd) __attribute__((always_inline)) {
     constexpr int NP = (D / 16) * QB;  // product i: k-step i / QB, query block i % QB
     auto rd = [&](int i) { return ld_lds16(tile + (rw ^ (16 * (i / QB))) + 32 * (i % QB) * D); };
+    if (negd == nullptr) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
+      for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
+    } else {
+      // registers 4 g .. 4 g + 3 of block qb hold queries 32 qb + 8 g + 4 hh + 0..3
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&negd[32 * qb + 8 * g + 4 * hh]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sd[qb][4 * g + e] = v[e];
+        }
+    }
     bf16x8 ar[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) ar[j] = rd(j);
@@ -293,17 +308,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int j = 0; j < 2 * QB; ++j) psb[kblk][j][lane] = opnd[j >> 1][j & 1];
   };
-  // dS-wave: dS = P (dP - D) -> opnd (bf16)
-  auto ds_phase = [&](const float* rsb, const u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
+  // dS-wave: dS = P (dP - D) -> opnd (bf16); sd already holds dP - D
+  auto ds_phase = [&](const u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
     u32x4 pp[2 * QB];
 #pragma unroll
     for (int j = 0; j < 2 * QB; ++j) pp[j] = psb[kblk][j][lane];
-    f32x4 d4[QB][4];  // D of queries 32 qb + 8 g + 4 hh + 0..3
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        d4[qb][g] = *reinterpret_cast<const f32x4*>(&rsb[BRB + 32 * qb + 8 * g + 4 * hh]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -313,7 +322,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const float p[4] = {lo16<F16>(w0), hi16<F16>(w0), lo16<F16>(w1), hi16<F16>(w1)};
         float ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ds[e] = p[e] * (sd[qb][4 * g + e] - d4[qb][g][e]);
+        for (int e = 0; e < 4; ++e) ds[e] = p[e] * sd[qb][4 * g + e];
         opnd[qb][g >> 1][2 * (g & 1)] = pack2<F16>(ds[0], ds[1]);
         opnd[qb][g >> 1][2 * (g & 1) + 1] = pack2<F16>(ds[2], ds[3]);
       }
@@ -349,15 +358,15 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if constexpr (p_role) {
       if constexpr (has_prev) second_product(obuf[bp]);  // dV += P_{s-1}^T dO_{s-1}
       if constexpr (has_cur) {
-        first_product(qbuf[b]);                           // S_s
+        first_product(qbuf[b], nullptr);                  // S_s
         p_phase(cur, rbuf[b], pbuf[b]);                   // P_s
       }
     } else {
       if constexpr (has_prev) {
-        ds_phase(rbuf[bp], pbuf[bp]);                     // dS_{s-1}
+        ds_phase(pbuf[bp]);                               // dS_{s-1}
         second_product(qbuf[bp]);                         // dK += dS_{s-1}^T Q_{s-1}
       }
-      if constexpr (has_cur) first_product(obuf[b]);     // dP_s
+      if constexpr (has_cur) first_product(obuf[b], rbuf[b] + BRB);  // dP_s - D
     }
     wait_vmem_all();  // the loads of step s + 1 have landed
     slot_barrier();
@@ -542,12 +551,15 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   }
   const float dval = pair_sum(dacc);
+  f32x16 negd16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd16[r] = -dval;
   const float l2 =
       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, (uint32_t)row * 4u, 0, 0)) * kLog2e;
   const float neg_l2 = -l2;
   if (hh == 0 && row < N) {
     rowstat[(size_t)bh * N + row] = l2;                     // LSE in base 2
-    rowstat[(size_t)BH * N + (size_t)bh * N + row] = dval;  // D
+    rowstat[(size_t)BH * N + (size_t)bh * N + row] = -dval; // -D
   }
 
   // ---- tile loads, straight from HBM into LDS: instruction n of a tile fills
@@ -594,13 +606,24 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   f32x16 s[BC / 32], dp[BC / 32];  // S^T, dP^T of the tile in flight
   u32x4 dsf[BC / 16];              // dS^T as B operands, 4 k-steps of 16 keys
 
-  // V(u): dS^T of key tile u from s, dp
+  // V(u): dS^T of key tile u from s, dp (= dP^T - D)
   auto vphase = [&](int u) __attribute__((always_inline)) {
     const int kv0 = u * BC;
     const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
-    // key kv0 + 32 kb + 8 (r / 4) + 4 hh + r % 4 is masked iff its offset
-    // 32 kb + 8 (r / 4) + r % 4 exceeds lim (one compare with a constant)
-    const int lim = (CAUSAL ? min(row, N - 1) : N - 1) - kv0 - 4 * hh;
+    if (need_mask) {
+      // Key kv0 + 32 kb + 8 (r / 4) + 4 hh + r % 4 is masked iff its offset
+      // 32 kb + 8 (r / 4) + r % 4 exceeds lim (one compare with a constant).
+      // A masked score becomes -inf, so P = 0 and dS = P (dP - D) = 0 exactly
+      // (dP is finite: past the sequence end K and V read as zeros). One
+      // branch around the whole tile: per-element branches would be flattened
+      // into selects that every tile pays for.
+      const int lim = (CAUSAL ? min(row, N - 1) : N - 1) - kv0 - 4 * hh;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : s[kb][r];
+    }
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -609,12 +632,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int u2 = 0; u2 < 2; ++u2) {
           const float p = fast_exp2(__builtin_fmaf(s[kb][r + u2], c_log2, neg_l2));
-          d2[u2] = p * (dp[kb][r + u2] - dval);
-        }
-        if (need_mask) {  // dS itself is zeroed: a masked tile may hold stale data
-#pragma unroll
-          for (int u2 = 0; u2 < 2; ++u2)
-            d2[u2] = 32 * kb + 8 * ((r + u2) >> 2) + ((r + u2) & 3) > lim ? 0.f : d2[u2];
+          d2[u2] = p * dp[kb][r + u2];
         }
         dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack2<F16>(d2[0], d2[1]);
       }
@@ -660,7 +678,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
         s[kb] = f32x16{};
-        dp[kb] = f32x16{};
+        dp[kb] = negd16;  // dP^T - D: every element of a lane is its query's
       }
       bf16x8 kr[R], vr[R];
 #pragma unroll

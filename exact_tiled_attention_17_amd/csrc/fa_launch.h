@@ -37,7 +37,7 @@ struct BwdArgs {
   float softmax_scale;
   hipStream_t stream;
   float* rowstat; // scratch of bwd_scratch_bytes: 2 x [B,H,N] float32 (LSE in base 2 for
-                  // every row, then D = dO . O), then the dK/dV partial sums if split
+                  // every row, then -D = -dO . O), then the dK/dV partial sums if split
   bool f16;       // element type of the 16-bit tensors: IEEE binary16 (true) or bf16
   int Hkv;        // K/V heads (K, V, dK, dV are [B,Hkv,N,d]); divides H
   bool no_split = false;  // never split the dK/dV work (scratch holds the row statistics only)
@@ -85,7 +85,7 @@ hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_mass(const MassArgs& a);
 hipError_t launch_quant(const QuantArgs& a);
 
-// float32 row statistics of the backward: LSE in base 2, then D, per query row
+// float32 row statistics of the backward: LSE in base 2, then -D, per query row
 // (padded to a multiple of 64 floats so that what follows stays 256-byte aligned).
 inline size_t rowstat_floats(int B, int H, int N) {
   return ((size_t)B * H * N * 2 + 63) / 64 * 64;
