@@ -258,6 +258,12 @@ int fa_quantize_e4m3(const void* X, void* codes, float* scales, int R, int N,
  * be finite with magnitudes below 2^120. Takes 2*B*Hkv*N*d bytes of scratch
  * (the dequantised K; Q is quantised as the forward loads it), stream-ordered
  * like fa_bwd's; FA_ERR_OUT_OF_MEMORY if it cannot be had.
+ * Speed: the products run on the bf16 matrix cores, so this call costs about
+ * as much as fa_fwd_ex plus the quantisation of K; it exists for its numerics.
+ * gfx950's only FP8 matrix instruction faster than bf16 (the 32x32x64 one,
+ * about twice the rate) scales per 32 values along the contraction, which a
+ * 16-wide block cannot use without re-encoding its codes; the 16-deep FP8
+ * instruction runs at the bf16 rate.
  */
 int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int H, int Hkv, int N, int d, int causal,
