@@ -75,7 +75,7 @@ struct BwdCfg {
 // the G / GS workgroups of a key block write float32 partial sums to `part`
 // and bwd_reduce_kernel adds them up; with GS == G (part == nullptr) the
 // workgroup writes dK, dV directly.
-template <int D, bool CAUSAL, bool F16>
+template <int D, bool CAUSAL, bool F16, bool PAIRS>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -104,8 +104,17 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int nkb = (N + BCB - 1) / BCB;
   const int BKV = BH / G;  // K/V heads
   const int S = G / GS;    // workgroups per key block
-  int hs, kb;
-  xcd_remap(blockIdx.x, nkb * BKV * S, nkb, hs, kb);  // causal: low key blocks (most work) first
+  // With PAIRS, workgroup w owns key blocks w and nkb - 1 - w (one block
+  // when they coincide) and its step pipeline runs from the first straight
+  // into the second. Under the causal mask every pair then has the same
+  // number of steps, and the workgroup's fixed costs (prologue, pipeline fill
+  // and drain) are paid once for both.
+  const int nwb = PAIRS ? (nkb + 1) / 2 : nkb;  // workgroups per (K/V head, split)
+  int hs, wb;
+  xcd_remap(blockIdx.x, nwb * BKV * S, nwb, hs, wb);  // causal: low key blocks (most work) first
+  const int kbA = wb;
+  const int kbB = PAIRS ? nkb - 1 - wb : wb;
+  const int nit = PAIRS && kbB != kbA ? 2 : 1;  // items (key blocks) of this workgroup
   const int bkv = hs / S;
   const int split = hs - bkv * S;
   const int qh0 = bkv * G + split * GS;  // first query head this workgroup serves
@@ -126,18 +135,20 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rK = make_rsrc(K + kvhead, head_bytes);
   const auto rV = make_rsrc(V + kvhead, head_bytes);
 
-  const int k0 = kb * BCB;
-  const int kw0 = k0 + 32 * kblk;  // this wave's first key
-  const int key = kw0 + l32;       // this lane's key (column of S)
+  // first key of item it's block, and of this wave's 32 keys in it
+  auto blk_k0 = [&](int it) { return (it ? kbB : kbA) * BCB; };
+  auto wave_k0 = [&](int it) { return blk_k0(it) + 32 * kblk; };
 
   // K rows (P-wave) or V rows (dS-wave) of this lane's key as B operands (0 past N)
   bf16x8 frag[D / 16];
-  {
-    const auto rF = pwave ? rK : rV;
+  const auto rF = pwave ? rK : rV;
+  auto load_frag = [&](int it) __attribute__((always_inline)) {
+    const int key = wave_k0(it) + l32;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
       frag[s] = as_bf16x8(buf_load16(rF, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
-  }
+  };
+  load_frag(0);
 
   // ---- step loads, straight from HBM into LDS: the Q and dO tiles of 64
   // queries (instruction n fills chunk positions [64 n, 64 n + 64), dealt
@@ -152,19 +163,28 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int m = 0; m < LM; ++m) src_w[m] = src(wave + 8 * m);
   const int nqt = (N + BRB - 1) / BRB;
-  const int i0 = CAUSAL ? k0 / BRB : 0;  // first query tile that sees the block's keys
-  const int nsteps = nqt - i0;           // steps per query head
-  // A step is (g, t): query head qh0 + g, query tile i0 + t. Steps run over
-  // t = 0 .. nsteps - 1 for g = 0 .. GS - 1; the padding steps after the last
-  // keep g = GS - 1 with t >= nsteps, so that all their queries are past N.
+  // first query tile that sees item it's keys, and its steps per query head
+  auto first_tile = [&](int it) { return CAUSAL ? blk_k0(it) / BRB : 0; };
+  auto nsteps = [&](int it) { return nqt - first_tile(it); };
+  // A step is (it, g, t): item it, query head qh0 + g, query tile
+  // first_tile(it) + t. Steps run over t = 0 .. nsteps(it) - 1 for
+  // g = 0 .. GS - 1, for it = 0 .. nit - 1; the padding steps after the last
+  // keep it = nit - 1, g = GS - 1 with t >= nsteps(it), so that all their
+  // queries are past N.
   struct Step {
-    int g, t;
+    int it, g, t;
   };
   auto advance = [&](Step p) __attribute__((always_inline)) {
     ++p.t;
-    if (p.t == nsteps && p.g + 1 < GS) {
-      p.t = 0;
-      ++p.g;
+    if (p.t == nsteps(p.it)) {
+      if (p.g + 1 < GS) {
+        p.t = 0;
+        ++p.g;
+      } else if (p.it + 1 < nit) {
+        p.t = 0;
+        p.g = 0;
+        ++p.it;
+      }
     }
     return p;
   };
@@ -174,7 +194,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto load_step = [&](Step p, __bf16* qd, __bf16* od, float* rsd) __attribute__((always_inline)) {
     const size_t qh = (size_t)(qh0 + p.g);  // query head
     const size_t head = qh * (size_t)N * D;
-    const int q0 = (i0 + p.t) * BRB;
+    const int q0 = (first_tile(p.it) + p.t) * BRB;
     const auto rQ = rows_rsrc(Q + head, q0, N, D * 2);
     const auto rdO = rows_rsrc(dO + head, q0, N, D * 2);
     // row statistics: LSE in base 2 for all rows, then -D = -dO . O for all rows
@@ -272,18 +292,19 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // query q0 + m (m = 32 qb + 8 g + 4 hh + e) contributes to this lane's key
   // iff (unsigned)(m + mbase) < mbound: the query exists and, if causal, is at
   // or after the key; a key past the end contributes nothing
-  auto mask_bounds = [&](int q0, int& mbase, unsigned& mbound) __attribute__((always_inline)) {
+  auto mask_bounds = [&](int q0, int key, int& mbase, unsigned& mbound) __attribute__((always_inline)) {
     const int qlo = CAUSAL ? key : 0;
     mbase = q0 - qlo;
     mbound = key < N ? (unsigned)(N - qlo) : 0u;
   };
   // P-wave: P = exp2(c S - LSE2) -> opnd (bf16) and to LDS for the partner
   auto p_phase = [&](Step p, const float* rsb, u32x4 (*psb)[2 * QB][64]) __attribute__((always_inline)) {
-    const int q0 = (i0 + p.t) * BRB;
+    const int q0 = (first_tile(p.it) + p.t) * BRB;
+    const int kw0 = wave_k0(p.it);
     const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + BRB > N);
     int mbase;
     unsigned mbound;
-    mask_bounds(q0, mbase, mbound);
+    mask_bounds(q0, kw0 + l32, mbase, mbound);
     f32x4 l4[QB][4];  // LSE2 of queries 32 qb + 8 g + 4 hh + 0..3, all read up front
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -340,36 +361,100 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // s mod 3, static in each copy); their count is padded to a multiple of 3
   // with steps past the end of the sequence, whose queries are all masked.
   // `cur` is step s, `nxt` step s + 1 (the one being loaded).
-  const int total = GS * nsteps;
+  const int total = GS * (nsteps(0) + (nit > 1 ? nsteps(1) : 0));
   const int last = 3 * ((total + 1) / 3) + 1;  // >= total, == 1 (mod 3)
   __bf16* const qbuf[3] = {qs0, qs1, qs2};
   __bf16* const obuf[3] = {os0, os1, os2};
   u32x4 (*const pbuf[3])[2 * QB][64] = {ps0, ps1, ps2};
   float* const rbuf[3] = {rs0, rs1, rs2};
+
+  // dV = dV_acc (P-waves) or dK = scale * dK_acc (dS-waves) of item it's keys
+  const float osc = pwave ? 1.f : scale;
+  auto flush = [&](int it) __attribute__((always_inline)) {
+    // Rows kw0 .. kw0 + 31 through a resource that starts at row kw0 and ends
+    // at row N: rows past N are dropped by the range check. Lane (l32, hh)
+    // writes column 32 b + l32 of rows 8 g + 4 hh + e (g = r / 4, e = r % 4):
+    // one offset register per g, the rest in the immediate.
+    const int kw0 = wave_k0(it);
+    if (part != nullptr) {
+      // float32 partial sums, [dV, dK][split][K/V head][N][D]
+      float* pout = part + ((size_t)(pwave ? 0 : S) + split) * BKV * (size_t)N * D + kvhead;
+      const auto rP = rows_rsrc(pout, kw0, N, D * 4);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t vo = (uint32_t)(((8 * g + 4 * hh) * D + l32) * 4);
+        asm volatile("" : "+v"(vo));  // formed here, not kept live across the loop
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b)
+            buf_store4(rP, vo + (uint32_t)((e * D + 32 * b) * 4),
+                       __builtin_bit_cast(uint32_t, acc_kd[b][4 * g + e] * osc));
+      }
+    } else {
+      const auto rO = rows_rsrc((pwave ? dV : dK) + kvhead, kw0, N, D * 2);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t vo = (uint32_t)(((8 * g + 4 * hh) * D + l32) * 2);
+        asm volatile("" : "+v"(vo));  // formed here, not kept live across the loop
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b)
+            buf_store2(rO, vo + (uint32_t)((e * D + 32 * b) * 2), to16<F16>(acc_kd[b][4 * g + e] * osc));
+      }
+    }
+  };
+
   // ROLE: P-wave (true) or dS-wave; each role runs its own straight-line copy
-  // of the schedule (same barriers), so neither carries the other's registers
-  auto slot = [&](auto ROLE, auto B3, auto HAS_PREV, auto HAS_CUR, int s, Step& cur,
+  // of the schedule (same barriers), so neither carries the other's registers.
+  // `cur`, `nxt` are steps s and s + 1, `prv_it` the item of step s - 1. In
+  // the slot where the first item's last step is s - 1 and the second item's
+  // first step is `cur`,
+  // the wave loads the second block's K or V rows at the start (their last
+  // reader, the first product of step s - 1, ran in the previous slot), and
+  // writes and clears its accumulators at the end (the second product of step
+  // s - 1 completed them).
+  auto slot = [&](auto ROLE, auto B3, auto HAS_PREV, auto HAS_CUR, int s, int& prv_it, Step& cur,
                   Step& nxt) __attribute__((always_inline)) {
     constexpr bool p_role = decltype(ROLE)::value;
     constexpr int b = decltype(B3)::value, bp = (b + 2) % 3, bn = (b + 1) % 3;
     constexpr bool has_prev = decltype(HAS_PREV)::value, has_cur = decltype(HAS_CUR)::value;
+    bool item_switch = false;
+    if constexpr (PAIRS && has_prev && has_cur) {
+      item_switch = prv_it != cur.it;
+      if (item_switch) load_frag(cur.it);
+    }
     if constexpr (has_cur)
       if (s + 1 < last) load_step(nxt, qbuf[bn], obuf[bn], rbuf[bn]);
     if constexpr (p_role) {
       if constexpr (has_prev) second_product(obuf[bp]);  // dV += P_{s-1}^T dO_{s-1}
-      if constexpr (has_cur) {
-        first_product(qbuf[b], nullptr);                  // S_s
-        p_phase(cur, rbuf[b], pbuf[b]);                   // P_s
-      }
     } else {
       if constexpr (has_prev) {
         ds_phase(pbuf[bp]);                               // dS_{s-1}
         second_product(qbuf[bp]);                         // dK += dS_{s-1}^T Q_{s-1}
       }
-      if constexpr (has_cur) first_product(obuf[b], rbuf[b] + BRB);  // dP_s - D
+    }
+    if constexpr (has_cur) {
+      if constexpr (p_role) {
+        first_product(qbuf[b], nullptr);                  // S_s
+        p_phase(cur, rbuf[b], pbuf[b]);                   // P_s
+      } else {
+        first_product(obuf[b], rbuf[b] + BRB);            // dP_s - D
+      }
     }
     wait_vmem_all();  // the loads of step s + 1 have landed
+    // The finished item's stores go out after that wait, so that they
+    // complete during the next slot instead of holding up this one.
+    if constexpr (PAIRS && has_prev && has_cur) {
+      if (item_switch) {
+        flush(prv_it);
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb) acc_kd[bb] = f32x16{};
+      }
+    }
     slot_barrier();
+    prv_it = cur.it;
     cur = nxt;
     nxt = advance(nxt);
   };
@@ -379,18 +464,19 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   using yes = std::true_type;
   using no = std::false_type;
   auto run = [&](auto ROLE) __attribute__((always_inline)) {
-    Step cur{0, 0};
+    int prv_it = 0;
+    Step cur{0, 0, 0};
     Step nxt = advance(cur);
-    slot(ROLE, c0{}, no{}, yes{}, 0, cur, nxt);
+    slot(ROLE, c0{}, no{}, yes{}, 0, prv_it, cur, nxt);
     for (int s = 1; s < last; s += 3) {
-      slot(ROLE, c1{}, yes{}, yes{}, s, cur, nxt);
-      slot(ROLE, c2{}, yes{}, yes{}, s + 1, cur, nxt);
-      slot(ROLE, c0{}, yes{}, yes{}, s + 2, cur, nxt);
+      slot(ROLE, c1{}, yes{}, yes{}, s, prv_it, cur, nxt);
+      slot(ROLE, c2{}, yes{}, yes{}, s + 1, prv_it, cur, nxt);
+      slot(ROLE, c0{}, yes{}, yes{}, s + 2, prv_it, cur, nxt);
     }
-    slot(ROLE, c1{}, yes{}, no{}, last, cur, nxt);
+    slot(ROLE, c1{}, yes{}, no{}, last, prv_it, cur, nxt);
   };
 
-  load_step(Step{0, 0}, qs0, os0, rs0);
+  load_step(Step{0, 0, 0}, qs0, os0, rs0);
   wait_vmem_all();
   __syncthreads();
   if (pwave)
@@ -398,28 +484,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   else
     run(no{});
 
-  // ---- epilogue: dV = dV_acc (P-waves), dK = scale * dK_acc (dS-waves) --------
-  const float osc = pwave ? 1.f : scale;
-  if (part != nullptr) {
-    // float32 partial sums, [dV, dK][split][K/V head][N][D]
-    float* pout = part + ((size_t)(pwave ? 0 : S) + split) * BKV * (size_t)N * D + kvhead;
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (kk < N) pout[(size_t)kk * D + 32 * b + l32] = acc_kd[b][r] * osc;
-      }
-    return;
-  }
-  uint16_t* out = reinterpret_cast<uint16_t*>(pwave ? dV : dK);
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kk < N) out[kvhead + (size_t)kk * D + 32 * b + l32] = to16<F16>(acc_kd[b][r] * osc);
-    }
+  // ---- epilogue: the last item's dV (P-waves) or dK (dS-waves) ---------------
+  flush(nit - 1);
 }
 
 // dV and dK from the float32 partial sums of S workgroups: `part` is
@@ -809,9 +875,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     const int G = a.H / a.Hkv;
     const int S = a.no_split ? 1 : dkdv_splits(a.B, a.H, a.Hkv, a.N, a.d);
     float* part = S > 1 ? a.rowstat + rowstat_floats(a.B, a.H, a.N) : nullptr;
-    const long long total = (long long)nkb * a.B * a.Hkv * S;
+    const long long blocks = (long long)nkb * a.B * a.Hkv * S;
+    // two key blocks per workgroup when that still leaves >= 1024 workgroups
+    const bool pairs = blocks >= 2 * kDkdvPairMinWorkgroups;
+    const long long total = pairs ? (long long)((nkb + 1) / 2) * a.B * a.Hkv * S : blocks;
     const hipError_t e = launch_kernel(
-        bwd_dkdv_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+        pairs ? bwd_dkdv_kernel<D, CAUSAL, F16, true> : bwd_dkdv_kernel<D, CAUSAL, F16, false>,
+        dim3((unsigned)total), dim3(C::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
         (const float*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, G, G / S,
         c_log2, a.softmax_scale, part);

@@ -188,6 +188,15 @@ __device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t r, uint32_t
                                            voff, 0, 0, 0);
 }
 
+// 2 or 4 bytes per lane through a buffer resource: a store whose per-lane
+// offset (plus the immediate) is past the resource's end writes nothing.
+__device__ __forceinline__ void buf_store2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }

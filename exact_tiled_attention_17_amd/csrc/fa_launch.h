@@ -97,6 +97,10 @@ inline size_t rowstat_floats(int B, int H, int N) {
 // attention: B * ceil(N / 128) workgroups), so the group is split until the
 // grid has 1024 workgroups (four per compute unit), each split writing
 // float32 partial sums (8 * S * B * Hkv * N * d bytes in all, kept under 1 GiB).
+// The dK/dV pass puts two key blocks in one workgroup (fewer, equally long
+// workgroups) only when at least this many workgroups remain.
+constexpr long long kDkdvPairMinWorkgroups = 1024;
+
 inline int dkdv_splits(int B, int H, int Hkv, int N, int d) {
   const int G = H / Hkv;
   const long long blocks = (long long)B * Hkv * ((N + 127) / 128);
