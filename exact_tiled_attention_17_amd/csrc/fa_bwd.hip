@@ -81,7 +81,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ rowstat, __bf16* __restrict__ dK,
                      __bf16* __restrict__ dV, int N, int BH, int G, int GS, float c_log2,
-                     float scale, float* __restrict__ part) {
+                     float scale, float* __restrict__ part, int ppw) {
   // BH query heads, BH / G K/V heads; K/V head j serves query heads G j .. G j + G - 1
   using C = BwdCfg<D>;
   constexpr int BCB = C::BCB, BRB = C::BRB, QB = C::QB, CH = C::CH, TI = C::TI;
@@ -104,17 +104,20 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int nkb = (N + BCB - 1) / BCB;
   const int BKV = BH / G;  // K/V heads
   const int S = G / GS;    // workgroups per key block
-  // With PAIRS, workgroup w owns key blocks w and nkb - 1 - w (one block
-  // when they coincide) and its step pipeline runs from the first straight
-  // into the second. Under the causal mask every pair then has the same
-  // number of steps, and the workgroup's fixed costs (prologue, pipeline fill
-  // and drain) are paid once for both.
-  const int nwb = PAIRS ? (nkb + 1) / 2 : nkb;  // workgroups per (K/V head, split)
+  // With PAIRS, key block p is paired with block nkb - 1 - p (the middle
+  // block of an odd count stands alone), workgroup w owns the ppw pairs
+  // starting at pair w * ppw, and its step pipeline runs through their
+  // blocks in turn (p, nkb - 1 - p, p + 1, ...). Under the causal mask every
+  // pair has the same number of steps, and the workgroup's fixed costs
+  // (prologue, pipeline fill and drain) are paid once for all its blocks.
+  const int npb = (nkb + 1) / 2;                           // pairs per (K/V head, split)
+  const int nwb = PAIRS ? (npb + ppw - 1) / ppw : nkb;      // workgroups per (K/V head, split)
   int hs, wb;
   xcd_remap(blockIdx.x, nwb * BKV * S, nwb, hs, wb);  // causal: low key blocks (most work) first
-  const int kbA = wb;
-  const int kbB = PAIRS ? nkb - 1 - wb : wb;
-  const int nit = PAIRS && kbB != kbA ? 2 : 1;  // items (key blocks) of this workgroup
+  const int p0 = wb * ppw;                        // first pair (PAIRS)
+  const int npw = PAIRS ? min(ppw, npb - p0) : 1;  // pairs of this workgroup (PAIRS)
+  // items (key blocks) of this workgroup
+  const int nit = PAIRS ? 2 * npw - ((nkb & 1) && p0 + npw == npb ? 1 : 0) : 1;
   const int bkv = hs / S;
   const int split = hs - bkv * S;
   const int qh0 = bkv * G + split * GS;  // first query head this workgroup serves
@@ -136,7 +139,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rV = make_rsrc(V + kvhead, head_bytes);
 
   // first key of item it's block, and of this wave's 32 keys in it
-  auto blk_k0 = [&](int it) { return (it ? kbB : kbA) * BCB; };
+  auto blk_k0 = [&](int it) {
+    if constexpr (!PAIRS) return wb * BCB;
+    const int p = p0 + (it >> 1);
+    return ((it & 1) ? nkb - 1 - p : p) * BCB;
+  };
   auto wave_k0 = [&](int it) { return blk_k0(it) + 32 * kblk; };
 
   // K rows (P-wave) or V rows (dS-wave) of this lane's key as B operands (0 past N)
@@ -361,7 +368,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // s mod 3, static in each copy); their count is padded to a multiple of 3
   // with steps past the end of the sequence, whose queries are all masked.
   // `cur` is step s, `nxt` step s + 1 (the one being loaded).
-  const int total = GS * (nsteps(0) + (nit > 1 ? nsteps(1) : 0));
+  int total = 0;
+  for (int it = 0; it < nit; ++it) total += GS * nsteps(it);
   const int last = 3 * ((total + 1) / 3) + 1;  // >= total, == 1 (mod 3)
   __bf16* const qbuf[3] = {qs0, qs1, qs2};
   __bf16* const obuf[3] = {os0, os1, os2};
@@ -877,14 +885,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     float* part = S > 1 ? a.rowstat + rowstat_floats(a.B, a.H, a.N) : nullptr;
     const long long blocks = (long long)nkb * a.B * a.Hkv * S;
     // two key blocks per workgroup when that still leaves >= 1024 workgroups
-    const bool pairs = blocks >= 2 * kDkdvPairMinWorkgroups;
-    const long long total = pairs ? (long long)((nkb + 1) / 2) * a.B * a.Hkv * S : blocks;
+    const int ppw = dkdv_pairs_per_workgroup(blocks, nkb);
+    const bool pairs = ppw > 0;
+    const long long total =
+        pairs ? (long long)(((nkb + 1) / 2 + ppw - 1) / ppw) * a.B * a.Hkv * S : blocks;
     const hipError_t e = launch_kernel(
         pairs ? bwd_dkdv_kernel<D, CAUSAL, F16, true> : bwd_dkdv_kernel<D, CAUSAL, F16, false>,
         dim3((unsigned)total), dim3(C::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
         (const float*)rowstat, (__bf16*)a.dK, (__bf16*)a.dV, a.N, a.B * a.H, G, G / S,
-        c_log2, a.softmax_scale, part);
+        c_log2, a.softmax_scale, part, pairs ? ppw : 1);
     if (e != hipSuccess) return e;
     if (S > 1) {
       const long long n = (long long)a.B * a.Hkv * a.N * D;

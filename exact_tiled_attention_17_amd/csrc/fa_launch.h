@@ -97,9 +97,24 @@ inline size_t rowstat_floats(int B, int H, int N) {
 // attention: B * ceil(N / 128) workgroups), so the group is split until the
 // grid has 1024 workgroups (four per compute unit), each split writing
 // float32 partial sums (8 * S * B * Hkv * N * d bytes in all, kept under 1 GiB).
-// The dK/dV pass puts two key blocks in one workgroup (fewer, equally long
-// workgroups) only when at least this many workgroups remain.
-constexpr long long kDkdvPairMinWorkgroups = 1024;
+// The dK/dV pass can give a workgroup pairs of key blocks (block p with
+// block nkb - 1 - p: equally long workgroups under the causal mask, fewer of
+// them). Pairs per workgroup: the largest of 4, 2, 1 that leaves at least
+// kDkdvMinWorkgroups workgroups for `blocks` key blocks (nkb per head), or 0
+// (one block per workgroup) if even single pairs would leave fewer.
+// More than one pair per workgroup measured no faster (two) or slower (four)
+// at 4x64x4096x128 and 8x64x2048x128 causal: each change of block costs a
+// slot's worth of waiting for the next block's rows.
+constexpr long long kDkdvMinWorkgroups = 1024;
+constexpr int kDkdvMaxPairsPerWorkgroup = 1;
+
+inline int dkdv_pairs_per_workgroup(long long blocks, int nkb) {
+  const long long heads = blocks / nkb;  // (batch, K/V head, split) triples
+  const int npb = (nkb + 1) / 2;
+  for (int m = kDkdvMaxPairsPerWorkgroup; m >= 1; m /= 2)
+    if (heads * ((npb + m - 1) / m) >= kDkdvMinWorkgroups && 2 * m <= nkb) return m;
+  return 0;
+}
 
 inline int dkdv_splits(int B, int H, int Hkv, int N, int d) {
   const int G = H / Hkv;

@@ -1,12 +1,12 @@
 """GPU parity for the dK/dV pass when it gives each workgroup two key blocks.
 
-When at least 2048 key-block workgroups would be launched, the dK/dV pass
-puts key blocks kb and nkb - 1 - kb into one workgroup and runs its step
-pipeline from the first block straight into the second: it loads the second
-block's K or V rows in the slot where the steps change blocks, writes and
-clears the first block's dK or dV at the end of that slot, and writes the
-second's after the sweep. With an odd block count the middle block has a
-workgroup of its own. The shapes below all take that path (block counts
+When the pairs of key blocks (block p with block nkb - 1 - p; the middle
+block of an odd count alone) number at least 1024 over all heads, the dK/dV
+pass gives each workgroup one or more pairs and runs its step pipeline from
+one block straight into the next: it loads the next block's K or V rows in
+the slot where the steps change blocks, writes and clears the finished
+block's dK or dV at the end of that slot, and writes the last block's after
+the sweep. The shapes below all take that path (block counts
 noted per case), with odd and even block counts, a ragged last block, d = 64
 and 128, both masks, and grouped K/V heads.
 
@@ -31,7 +31,7 @@ from tests.gpu_util import GRAD_RTOL, LSE_ATOL, O_ATOL, announce, max_abs, rel_t
 
 pytestmark = pytest.mark.gpu
 
-CASES = [  # B, H, Hkv, N, d, causal   (key blocks = B * Hkv * ceil(N / 128))
+CASES = [  # B, H, Hkv, N, d, causal   (key blocks = B * Hkv * nkb, nkb = ceil(N / 128))
     (2, 72, 72, 1920, 128, True),     # 2160 blocks, 15 per head (odd: a middle block alone)
     (2, 72, 72, 1920, 128, False),
     (1, 128, 128, 2113, 128, True),   # 2176 blocks, 17 per head, last block 65 keys
@@ -51,7 +51,8 @@ def _grad_err(mine, ref):
 @pytest.mark.parametrize("B,H,Hkv,N,d,causal", CASES)
 def test_paired_key_blocks(fa, B, H, Hkv, N, d, causal):
     import torch
-    assert B * Hkv * ((N + 127) // 128) >= 2048  # the shapes must take the paired path
+    nkb = (N + 127) // 128
+    assert B * Hkv * ((nkb + 1) // 2) >= 1024  # the shapes must take the paired path
     seed = 7700 + N + 3 * H + Hkv + d + int(causal)
     announce(f"dkdv pairs B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} seed={seed}")
     x = ai.make_qkv(B, H, N, d, seed, with_do=True, Hkv=Hkv)
