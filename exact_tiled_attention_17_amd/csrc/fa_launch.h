@@ -103,8 +103,7 @@ inline size_t rowstat_floats(int B, int H, int N) {
 // kDkdvMinWorkgroups workgroups for `blocks` key blocks (nkb per head), or 0
 // (one block per workgroup) if even single pairs would leave fewer.
 // More than one pair per workgroup measured no faster (two) or slower (four)
-// at 4x64x4096x128 and 8x64x2048x128 causal: each change of block costs a
-// slot's worth of waiting for the next block's rows.
+// at 4x64x4096x128 and 8x64x2048x128 causal.
 constexpr long long kDkdvMinWorkgroups = 1024;
 constexpr int kDkdvMaxPairsPerWorkgroup = 1;
 
