@@ -25,5 +25,7 @@ from .fp8 import (  # noqa: F401
     e4m3_encode,
     e4m3_round,
     fp8_attention_forward,
+    mx_fp8_attention_forward,
     quantize_e4m3_blocks,
+    quantize_e4m3_rows32,
 )

@@ -9,6 +9,14 @@ and of K is quantised to E4M3 with a scale factor of its own. Item 2, Design,
 Step 1 fixes the cast: a saturating clamp to [-448, 448] before encoding E4M3
 (448 being E4M3's largest finite value).
 
+Two block shapes are provided. The 16 x 16 blocks follow the FP8 path's own
+words. The 1 x 32 blocks (one token row by 32 consecutive head-dim columns,
+a power-of-two scale per block: the OCP MX block layout) are an alternative
+reading: the same spec names MX block-wise quantisation among its existing
+FP8 pieces (Item 2, Current state), and the FP8 path is there for roughly
+twice the matrix throughput, which FP8 matrix units that scale per 32
+values along the contraction only give to blocks of that width.
+
 Readings where the pages are silent (each listed in the design notes):
   * a block is 16 consecutive token rows x 16 consecutive head-dim columns of
     one head's [N, d] matrix; the last row block of a head may be shorter;
@@ -32,6 +40,7 @@ from .attention import attention_forward
 
 E4M3_MAX = 448.0
 BLOCK = 16
+MX_BLOCK = 32
 E_MIN = -100
 
 
@@ -128,3 +137,37 @@ def fp8_attention_forward(q, k, v, causal: bool, scale: float):
     _, _, qd = quantize_e4m3_blocks(q.reshape(B * H, N, d))
     _, _, kd = quantize_e4m3_blocks(k.reshape(B * Hkv, N, d))
     return attention_forward(qd.reshape(q.shape), kd.reshape(k.shape), v, causal, scale)
+
+
+def quantize_e4m3_rows32(x: np.ndarray):
+    """Quantise [R, N, d] (float64) per 1 x 32 block: one row, columns
+    32 c .. 32 c + 31, with the same scale rule and rounding as the 16 x 16
+    blocks.
+
+    Returns (codes uint8 [R, N, d], exponents int64 [R, N, d/32],
+    dequantised float64 [R, N, d] = decode(codes) * 2^e).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R, N, d = x.shape
+    if d % MX_BLOCK:
+        raise ValueError("d must be a multiple of 32")
+    nb = d // MX_BLOCK
+    blk = x.reshape(R, N, nb, MX_BLOCK)
+    e = block_exponent(np.abs(blk).max(axis=3))            # [R, N, nb]
+    v = e4m3_round(np.ldexp(blk, -e[..., None]))
+    codes = e4m3_encode(v).reshape(R, N, d)
+    deq = np.ldexp(v, e[..., None]).reshape(R, N, d)
+    return codes, e.astype(np.int64), deq
+
+
+def mx_fp8_attention_forward(q, k, v, causal: bool, scale: float):
+    """O and LSE of the FP8 path under the 1 x 32 block reading: exact
+    attention on Q, K quantised per row and 32 columns.
+
+    q: [B,H,N,d], k, v: [B,Hkv,N,d] float64 (the decoded 16-bit inputs).
+    """
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    qd = quantize_e4m3_rows32(q.reshape(B * H, N, d))[2].reshape(q.shape)
+    kd = quantize_e4m3_rows32(k.reshape(B * Hkv, N, d))[2].reshape(k.shape)
+    return attention_forward(qd, kd, v, causal, scale)

@@ -598,6 +598,103 @@ def check_fp8_forward(orc):
         assert np.array_equal(o8c, o8) and np.array_equal(o8d, o8)
 
 
+# --- C24: 1 x 32 block quantisation: geometry, exponents, error, fixed points --
+def check_rows32_quantisation(orc):
+    """Each 1 x 32 block (one row, 32 aligned columns) is quantised on its
+    own: its exponent is the closed-form one of its own amax (so a block
+    whose largest magnitude is 448 * 2^k gets exactly k), changing one
+    element moves only its block, the error is at most half an E4M3 step at
+    the block's scale, values on a block's grid are kept, and a 16 x 16
+    geometry would give other exponents on the same input."""
+    rng = _rng(34)
+    R, N, d = 2, 7, 128
+    x = rng.standard_normal((R, N, d)) * np.exp(rng.uniform(-4, 4, (R, N, 1)))
+    codes, expo, deq = orc.quantize_e4m3_rows32(x)
+    assert codes.shape == (R, N, d) and expo.shape == (R, N, 4)
+    for r in range(R):
+        for n in range(N):
+            for c in range(4):
+                blk = x[r, n, 32 * c:32 * c + 32]
+                assert expo[r, n, c] == orc.block_exponent(np.array([np.abs(blk).max()]))[0]
+                top = np.abs(blk).max() / 2.0 ** expo[r, n, c]
+                assert 224.0 < top <= 448.0
+    # closed form: a block whose amax is exactly 448 * 2^k
+    z = rng.uniform(-1, 1, (1, 3, 64))
+    for n, k in enumerate((-9, 0, 5)):
+        z[0, n, :32] *= 448.0 * 2.0 ** k
+        z[0, n, 7] = -448.0 * 2.0 ** k
+        z[0, n, 32:] = 0.0
+    _, ez, dz = orc.quantize_e4m3_rows32(z)
+    assert ez[0, :, 0].tolist() == [-9, 0, 5] and (ez[0, :, 1] == 0).all() and (dz[0, :, 32:] == 0).all()
+    # error bound
+    scl = 2.0 ** np.repeat(expo, 32, axis=2)
+    y, yq = x / scl, deq / scl
+    _, ex = np.frexp(np.abs(y))
+    step = 2.0 ** (np.maximum(ex - 1, -6) - 3)
+    assert np.all(np.abs(y - yq) <= step / 2)
+    # locality: one element moves only its own 1 x 32 block
+    x2 = x.copy()
+    x2[1, 4, 70] *= 1000.0
+    c2, e2, _ = orc.quantize_e4m3_rows32(x2)
+    changed = np.argwhere(c2 != codes)
+    assert len(changed) > 0 and all(r == 1 and n == 4 and 64 <= c < 96 for r, n, c in changed)
+    assert np.argwhere(e2 != expo).tolist() == [[1, 4, 2]]
+    # fixed points and idempotence
+    grid = orc.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    w = rng.choice(np.concatenate([grid, -grid]), size=(1, 4, 64)) * 2.0 ** 3
+    w[..., ::32] = 448.0 * 2.0 ** 3
+    wc, we, wd = orc.quantize_e4m3_rows32(w)
+    assert np.array_equal(wd, w) and (we == 3).all()
+    assert np.array_equal(orc.quantize_e4m3_rows32(deq)[2], deq)
+    # the geometry matters: 16 x 16 blocks pool 16 rows' magnitudes
+    x3 = np.ones((1, 16, 32))
+    x3[0, 0, 0] = 448.0 * 2.0 ** 6
+    assert orc.quantize_e4m3_rows32(x3)[1][0, 1:, 0].tolist() == [-8] * 15
+    assert orc.quantize_e4m3_blocks(x3)[1][0, 0, 0] == 6
+
+
+# --- C25: the 1 x 32 FP8 forward is exact attention on its dequantised operands
+def check_mx_fp8_forward(orc):
+    """Inputs on their 1 x 32 blocks' grids pass through unchanged (the
+    forward equals the plain one there); on general inputs the result is the
+    plain forward of the dequantised Q and K, and differs from the plain
+    forward by no more than the quantisation explains; quantising is
+    idempotent, so both operands are quantised exactly once."""
+    rng = _rng(35)
+    grid = orc.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    for causal in (False, True):
+        q = rng.choice(np.concatenate([grid, -grid]), size=(1, 2, 20, 64)) * 2.0 ** -7
+        k = rng.choice(np.concatenate([grid, -grid]), size=(1, 1, 20, 64)) * 2.0 ** -7
+        q[..., ::32] = 448.0 * 2.0 ** -7
+        k[..., ::32] = 448.0 * 2.0 ** -7
+        v = rng.standard_normal((1, 1, 20, 64))
+        o8, l8 = orc.mx_fp8_attention_forward(q, k, v, causal, 0.3)
+        o, lse = orc.attention_forward(q, k, v, causal, 0.3)
+        assert np.array_equal(o8, o) and np.array_equal(l8, lse)
+        q = rng.standard_normal((2, 4, 33, 64))
+        k = rng.standard_normal((2, 2, 33, 64))
+        v = rng.standard_normal((2, 2, 33, 64))
+        o8, l8 = orc.mx_fp8_attention_forward(q, k, v, causal, 0.3)
+        qd = orc.quantize_e4m3_rows32(q.reshape(8, 33, 64))[2].reshape(q.shape)
+        kd = orc.quantize_e4m3_rows32(k.reshape(4, 33, 64))[2].reshape(k.shape)
+        o_d, l_d = orc.attention_forward(qd, kd, v, causal, 0.3)
+        assert np.array_equal(o8, o_d) and np.array_equal(l8, l_d)
+        o, lse = orc.attention_forward(q, k, v, causal, 0.3)
+        kr = np.repeat(k, 2, axis=1)
+        dkr = np.repeat(np.abs(kd - k), 2, axis=1)
+        ds = 0.3 * (np.abs(qd - q) @ np.abs(kr).swapaxes(-1, -2) + np.abs(q) @ dkr.swapaxes(-1, -2))
+        bound = ds.max()
+        assert 0 < np.abs(l8 - lse).max() <= bound
+        assert np.abs(o8 - o).max() <= 2 * bound * np.abs(v).max()
+        o8b, l8b = orc.mx_fp8_attention_forward(qd, kd, v, causal, 0.3)
+        assert np.array_equal(o8b, o8) and np.array_equal(l8b, l8)
+        # and it is not the 16 x 16 path: with row magnitudes that differ,
+        # 16 x 16 blocks share one scale across rows, 1 x 32 blocks do not
+        qs = q * np.exp(rng.uniform(-3, 3, (2, 4, 33, 1)))
+        assert not np.array_equal(orc.mx_fp8_attention_forward(qs, k, v, causal, 0.3)[0],
+                                  orc.fp8_attention_forward(qs, k, v, causal, 0.3)[0])
+
+
 ALL_CHECKS = [
     check_identical_keys,
     check_single_token,
@@ -622,4 +719,6 @@ ALL_CHECKS = [
     check_block_exponent,
     check_block_quantisation,
     check_fp8_forward,
+    check_rows32_quantisation,
+    check_mx_fp8_forward,
 ]

@@ -63,6 +63,13 @@ MUTANTS = {
                               "deq[:, rows, cols] = v"),
     "fp8_forward_unquantised_k": ("fp8", "return attention_forward(qd.reshape(q.shape), kd.reshape(k.shape), v, causal, scale)",
                                   "return attention_forward(qd.reshape(q.shape), k, v, causal, scale)"),
+    "rows32_amax_whole_row": ("fp8", "e = block_exponent(np.abs(blk).max(axis=3))            # [R, N, nb]",
+                              "e = block_exponent(np.abs(blk).max(axis=(2, 3)))[..., None] + 0 * np.abs(blk).max(axis=3).astype(np.int64)"),
+    "rows32_blocks_of_16": ("fp8", "blk = x.reshape(R, N, nb, MX_BLOCK)", "blk = x.reshape(R, N, 2 * nb, 16)[:, :, ::2, :].repeat(1, axis=2).reshape(R, N, nb, 16).repeat(2, axis=3)"),
+    "rows32_dequant_without_scale": ("fp8", "deq = np.ldexp(v, e[..., None]).reshape(R, N, d)",
+                                     "deq = v.reshape(R, N, d)"),
+    "mx_forward_unquantised_q": ("fp8", "return attention_forward(qd, kd, v, causal, scale)",
+                                 "return attention_forward(q, kd, v, causal, scale)"),
     "f16_decoded_as_bf16": ("return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)",
                             "return bf16_bits_to_f64(bits)"),
 }
