@@ -2,10 +2,12 @@
 
 A thin binding of ``libfa.so`` (C ABI in ``include/fa.h``). The functions
 ``fa_fwd``, ``fa_bwd``, ``fa_fwd_ex``, ``fa_bwd_ex``, ``fa_bwd_noalloc``,
-``fa_key_mass``, ``fa_quantize_e4m3``, ``fa_fwd_fp8`` and ``fa_status_string`` mirror the C
+``fa_key_mass``, ``fa_quantize_e4m3``, ``fa_fwd_fp8``, ``fa_quantize_mx_e4m3``,
+``fa_fwd_mxfp8`` and ``fa_status_string`` mirror the C
 entry points one to one (raw device pointers as Python ints, ``stream`` as a
 hipStream_t handle). ``forward``, ``backward``, ``key_mass``,
-``quantize_e4m3`` and ``forward_fp8`` are conveniences over torch tensors:
+``quantize_e4m3``, ``forward_fp8``, ``quantize_mx_e4m3`` and ``forward_mxfp8`` are
+conveniences over torch tensors:
 they check dtypes and shapes, allocate outputs with torch and pass
 ``data_ptr()`` and the current stream; every step of the computation runs in
 the library's HIP kernels. There is no fallback: if the library is missing
@@ -23,8 +25,9 @@ import os
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_noalloc", "fa_key_mass",
            "fa_quantize_e4m3", "FA_NOALLOC_MAX_ROWS",
-           "fa_fwd_fp8", "fa_status_string", "fa_last_hip_error",
-           "forward", "backward", "key_mass", "quantize_e4m3", "forward_fp8", "load", "FAError", "LIB_PATH", "FA_DTYPE_BF16", "FA_DTYPE_F16"]
+           "fa_fwd_fp8", "fa_quantize_mx_e4m3", "fa_fwd_mxfp8", "fa_status_string", "fa_last_hip_error",
+           "forward", "backward", "key_mass", "quantize_e4m3", "forward_fp8", "quantize_mx_e4m3",
+           "forward_mxfp8", "load", "FAError", "LIB_PATH", "FA_DTYPE_BF16", "FA_DTYPE_F16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -87,6 +90,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fa_quantize_e4m3.restype = ci
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
     lib.fa_fwd_fp8.restype = ci
+    lib.fa_quantize_mx_e4m3.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
+    lib.fa_quantize_mx_e4m3.restype = ci
+    lib.fa_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.fa_fwd_mxfp8.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -151,6 +158,17 @@ def fa_fwd_fp8(Q, K, V, O, LSE, B, H, Hkv, N, d, causal, softmax_scale, stream) 
     """C ``fa_fwd_fp8``: the forward with Q and K quantised to E4M3 per 16 x 16 block."""
     return load().fa_fwd_fp8(Q, K, V, O, LSE or None, B, H, Hkv, N, d, int(causal),
                              float(softmax_scale), stream or None)
+
+
+def fa_quantize_mx_e4m3(X, codes, scales, R, N, d, dtype, stream) -> int:
+    """C ``fa_quantize_mx_e4m3``: E4M3 codes and E8M0 scale bytes per 1 x 32 block."""
+    return load().fa_quantize_mx_e4m3(X, codes, scales, R, N, d, int(dtype), stream or None)
+
+
+def fa_fwd_mxfp8(Q, K, V, O, LSE, B, H, Hkv, N, d, causal, softmax_scale, stream) -> int:
+    """C ``fa_fwd_mxfp8``: the forward with Q and K quantised to E4M3 per 1 x 32 block."""
+    return load().fa_fwd_mxfp8(Q, K, V, O, LSE or None, B, H, Hkv, N, d, int(causal),
+                               float(softmax_scale), stream or None)
 
 
 def _dtype_code(t):
@@ -325,4 +343,59 @@ def forward_fp8(q, k, v, causal: bool = False, scale: float | None = None, *, ou
                         _scale(scale, d), stream)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_fp8")
+    return out, lse
+
+
+def quantize_mx_e4m3(x):
+    """E4M3 codes (uint8, same shape) and E8M0 scale bytes (uint8 [..., N, d/32]; byte s
+    means 2^(s - 127)) of a bf16 or float16 tensor [..., N, d], quantised per 1 x 32 block
+    (one row, 32 consecutive columns)."""
+    import torch
+    if x.dim() < 2:
+        raise ValueError("x must be [..., seq_len, head_dim]")
+    N, d = int(x.shape[-2]), int(x.shape[-1])
+    R = int(x.numel() // (N * d)) if x.numel() else 0
+    code = _dtype_code(x)
+    _check("x", x, tuple(x.shape), x.dtype, x.device)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty((*x.shape[:-1], d // 32), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = fa_quantize_mx_e4m3(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), R, N, d, code,
+                                 stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_mx_e4m3")
+    return codes, scales
+
+
+def forward_mxfp8(q, k, v, causal: bool = False, scale: float | None = None, *, out=None, lse=None,
+                  need_lse: bool = True):
+    """O, LSE of the FP8 path under the 1 x 32 block reading: q, k quantised to E4M3 per row
+    and 32 columns, S = Q K^T on the scaled FP8 matrix instruction (bf16 tensors shaped as in
+    ``forward``)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, seq_len, head_dim]")
+    B, H, N, d = q.shape
+    Hkv = _kv_heads(H, k)
+    dev = q.device
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"the FP8 path takes bfloat16 tensors, got {q.dtype}")
+    _check("q", q, (B, H, N, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, Hkv, N, d), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("out", out, (B, H, N, d), q.dtype, dev)
+    if need_lse:
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        _check("lse", lse, (B, H, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = fa_fwd_mxfp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if need_lse else None, B, H, Hkv, N, d, causal,
+                          _scale(scale, d), stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_mxfp8")
     return out, lse

@@ -200,7 +200,51 @@ int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
   hipError_t e = fa::launch_quant(fa::QuantArgs{K, nullptr, nullptr, kd, B * Hkv, N, d, s, false});
   if (e == hipSuccess) {
     fa::FwdArgs fa_args{Q, kd, V, O, LSE, B, H, N, d, causal != 0, softmax_scale, s, false, Hkv};
-    fa_args.quant_q = true;
+    fa_args.fp8 = 1;
+    e = fa::launch_fwd(fa_args);
+  }
+  const hipError_t f = hipFreeAsync(scratch, s);
+  return hip_status(e != hipSuccess ? e : f, FA_ERR_HIP);
+}
+
+int fa_quantize_mx_e4m3(const void* X, void* codes, void* scales, int R, int N, int d, int dtype,
+                        void* stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
+  if (R < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)R * N * d >= (1LL << 40)) return FA_ERR_INVALID_ARG;
+  int st = check_tensor(X);
+  if (st != FA_OK) return st;
+  if (codes == nullptr || !aligned(codes, 16) || scales == nullptr) return FA_ERR_INVALID_ARG;
+  fa::QuantMxArgs a{X, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), R, N, d,
+                    reinterpret_cast<hipStream_t>(stream), dtype == FA_DTYPE_F16, d / 32};
+  return hip_status(fa::launch_quant_mx(a), FA_ERR_HIP);
+}
+
+int fa_fwd_mxfp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                 int Hkv, int N, int d, int causal, float softmax_scale, void* stream) {
+  int st = check_common(B, H, Hkv, N, d, causal, softmax_scale);
+  if (st != FA_OK) return st;
+  for (const void* p : {Q, K, V, (const void*)O})
+    if ((st = check_tensor(p)) != FA_OK) return st;
+  if (LSE != nullptr && !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // K is quantised into scratch: its codes, then a 4-byte word of scale bytes
+  // per key (d / 32 of them used); Q is quantised by the forward as it loads it
+  const size_t code_bytes = (size_t)B * Hkv * N * d;
+  const size_t scale_bytes = (size_t)B * Hkv * N * 4;
+  void* scratch = nullptr;
+  const hipError_t m = hipMallocAsync(&scratch, code_bytes + scale_bytes, s);
+  if (m != hipSuccess || scratch == nullptr)
+    return hip_status(m == hipSuccess ? hipErrorOutOfMemory : m, FA_ERR_OUT_OF_MEMORY);
+  uint8_t* kc = static_cast<uint8_t*>(scratch);
+  uint8_t* ks = kc + code_bytes;
+  hipError_t e = fa::launch_quant_mx(fa::QuantMxArgs{K, kc, ks, B * Hkv, N, d, s, false, 4});
+  if (e == hipSuccess) {
+    fa::FwdArgs fa_args{Q, kc, V, O, LSE, B, H, N, d, causal != 0, softmax_scale, s, false, Hkv};
+    fa_args.fp8 = 2;
+    fa_args.k_scales = ks;
     e = fa::launch_fwd(fa_args);
   }
   const hipError_t f = hipFreeAsync(scratch, s);

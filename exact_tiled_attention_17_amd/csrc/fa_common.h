@@ -16,6 +16,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -88,6 +89,19 @@ __device__ __forceinline__ uint32_t e4m3_deq2_bf16(uint32_t w, int b, int e) {
   const float a = __builtin_amdgcn_ldexpf(e4m3_byte(w, b), e);
   const float c = __builtin_amdgcn_ldexpf(e4m3_byte(w, b + 1), e);
   return (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, c) & 0xFFFF0000u);
+}
+
+// S^T += A B on the scaled 32x32x64 FP8 matrix instruction, both operands
+// E4M3 codes. Lane layout (gfx950, measured by an in-bounds probe): lane l
+// holds row (A) or column (B) l % 32; its bytes 0..15 are k = 16 (l / 32) +
+// 0..15 and bytes 16..31 are k = 32 + 16 (l / 32) + 0..15. The products of
+// k-block kb (k = 32 kb .. 32 kb + 31) of row i (column j) are scaled by the
+// E8M0 byte OP of lane i + 32 kb's scale word (j + 32 kb's for B): 2^(byte -
+// 127). C starts at zero when FIRST.
+template <int OP, bool FIRST>
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, FIRST ? f32x16{} : c, 0, 0, OP, (int)sa,
+                                                         OP, (int)sb);
 }
 
 // Lanes l and l ^ 32 exchange values; returns (own, partner) in some order,

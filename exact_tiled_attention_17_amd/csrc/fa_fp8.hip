@@ -1,8 +1,9 @@
 // FP8 (E4M3) path: Q and K quantised per 16 x 16 block before S = Q K^T
 // ("GPU Performance Optimization Batch 1 - Design Spec", Item 3, Design,
 // optional FP8 path; Item 2, Design, Step 1 for the saturating E4M3 cast).
-// This file holds the quantisation kernel (fa_quantize_e4m3, and K for
-// fa_fwd_fp8); the forward quantises Q itself as it loads it (fa_fwd.hip).
+// This file holds the quantisation kernels (fa_quantize_e4m3, and K for
+// fa_fwd_fp8; fa_quantize_mx_e4m3, and K for fa_fwd_mxfp8, the 1 x 32 block
+// reading); the forward quantises Q itself as it loads it (fa_fwd.hip).
 //
 // A block is 16 token rows x 16 head-dim columns of one head. Its scale is
 // the power of two 2^e with the smallest e such that the block's largest
@@ -94,6 +95,56 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const __bf16* __restric
   }
   if (scales != nullptr && lane < CPR && (lane & 1) == 0)
     scales[((size_t)r * nrb + rb) * (D / 16) + lane / 2] = __builtin_amdgcn_ldexpf(1.f, e);
+}
+
+// 1 x 32 blocks (one row, 32 aligned columns; the same scale rule and
+// rounding): thread g quantises block g, which is elements [32 g, 32 g + 32)
+// of the [R, N, d] input (64 contiguous bytes), and writes its 32 codes and
+// its scale byte 127 + e (E8M0: 2^(byte - 127)) at byte c of its row's
+// scale_stride bytes (c = the block's index in the row, of bpr = d / 32). No
+// shuffles: a block is one thread's.
+template <bool F16>
+__global__ __launch_bounds__(256) void quant_mx_kernel(const __bf16* __restrict__ X,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, long long nblk,
+                                                       int bpr, int scale_stride) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= nblk) return;
+  const __bf16* src = X + g * 32;
+  float x[32];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const u32x4 w = ld_global16(src + 8 * v);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      x[8 * v + 2 * m] = lo16<F16>(w[m]);
+      x[8 * v + 2 * m + 1] = hi16<F16>(w[m]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const int e = e4m3_block_exp(amax);
+  u32x4 c0, c1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c0[j] = e4m3_codes4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], e);
+    c1[j] = e4m3_codes4(x[16 + 4 * j], x[17 + 4 * j], x[18 + 4 * j], x[19 + 4 * j], e);
+  }
+  *reinterpret_cast<u32x4*>(codes + g * 32) = c0;
+  *reinterpret_cast<u32x4*>(codes + g * 32 + 16) = c1;
+  const long long row = g / bpr;
+  scales[row * scale_stride + (g - row * bpr)] = (uint8_t)(127 + e);
+}
+
+hipError_t launch_quant_mx(const QuantMxArgs& a) {
+  const long long nblk = (long long)a.R * a.N * (a.d / 32);
+  const dim3 grid((unsigned)((nblk + 255) / 256));
+  if (a.f16)
+    return launch_kernel(quant_mx_kernel<true>, grid, dim3(256), a.stream, (const __bf16*)a.X, a.codes,
+                         a.scales, nblk, a.d / 32, a.scale_stride);
+  return launch_kernel(quant_mx_kernel<false>, grid, dim3(256), a.stream, (const __bf16*)a.X, a.codes,
+                       a.scales, nblk, a.d / 32, a.scale_stride);
 }
 
 template <int D, bool F16>

@@ -86,13 +86,20 @@ __device__ __forceinline__ int voff(int r, int col) {  // element offset of (r, 
 // (plus S_0 and softmax(S_0) up front). Group B (waves 4..7) runs one phase
 // behind group A (waves 0..3); each phase ends at a workgroup barrier, so on
 // every SIMD one wave's softmax runs while the other wave's products do.
-// QQ: the FP8 path's Q, quantised to E4M3 per 16 x 16 block (scale rule in
-// fa_common.h) and dequantised in registers as it is loaded (bf16 only).
-template <int D, bool CAUSAL, bool F16, bool QQ>
+// QM, the FP8 paths (bf16 only):
+//  1: Q quantised to E4M3 per 16 x 16 block (scale rule in fa_common.h) and
+//     dequantised in registers as it is loaded; K arrives dequantised.
+//  2: the 1 x 32 block reading: Q quantised per row and 32 columns in
+//     registers and kept as E4M3 codes; K arrives as codes with E8M0 scale
+//     bytes (Ksc: 4 bytes per key, d / 32 of them used); S^T = K Q^T runs on
+//     the scaled 32x32x64 FP8 matrix instruction, which applies both block
+//     scales, at twice the bf16 rate.
+template <int D, bool CAUSAL, bool F16, int QM>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                float* __restrict__ LSE, int N, int BH, int G, float c_log2) {
+                float* __restrict__ LSE, int N, int BH, int G, float c_log2,
+                const uint8_t* __restrict__ Ksc) {
   // BH query heads; query head bh reads K/V head bh / G (G query heads per
   // K/V head: 1 for multi-head attention, H for multi-query attention)
   using C = FwdCfg<D>;
@@ -113,6 +120,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) __bf16 ks1[BC * KST];
   __shared__ __attribute__((aligned(16))) __bf16 vs0[BC * D];    // V tiles, swizzled
   __shared__ __attribute__((aligned(16))) __bf16 vs1[BC * D];
+  // QM 2: the K tiles' scale words (one per key) beside the code tiles, which
+  // use the first BC * (D + 16) bytes of ks0 / ks1
+  __shared__ __attribute__((aligned(16))) uint32_t ksc0[QM == 2 ? BC : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t ksc1[QM == 2 ? BC : 1];
 
   const int nq = (N + BR - 1) / BR;
   int bh, qt;
@@ -153,17 +164,56 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int jw_last = !wave_active ? -1 : CAUSAL ? min(wrow0 + 31, N - 1) / BC : T - 1;
 
   // ---- Q^T operand: lane holds row `row`, d = 16 s + 8 hh .. +7 (0 past N) --
-  bf16x8 qf[D / 16];
+  bf16x8 qf[QM == 2 ? 1 : D / 16];
+  if constexpr (QM != 2) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
-  if constexpr (QQ) {
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
+  }
+  // QM 2: Q^T as E4M3 codes, the B operand of the scaled FP8 product. For the
+  // 64-column step st the lane holds columns 64 st + 16 hh .. + 15 (bytes
+  // 0..15, block 2 st) and 64 st + 32 + 16 hh .. + 15 (bytes 16..31, block
+  // 2 st + 1); each block of the row is split over the lane pair (hh = 0, 1),
+  // so its amax takes one swap. The scale word's byte 2 st is the lane's own
+  // block exponent for the instruction (block 2 st + hh), plus 127.
+  constexpr int NST = D / 64;
+  i32x8 qf8[QM == 2 ? NST : 1];
+  uint32_t qsw = 0;
+  if constexpr (QM == 2) {
+    static_assert(!F16, "the FP8 paths take bf16 inputs");
+    uint32_t sw = 0;
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint32_t off = (uint32_t)row * (D * 2) + (64 * st + 32 * hb + 16 * hh) * 2;
+        const u32x4 w0 = buf_load16(rQ, off), w1 = buf_load16(rQ, off + 16);
+        float x[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          x[2 * m] = lo16<false>(w0[m]);
+          x[2 * m + 1] = hi16<false>(w0[m]);
+          x[8 + 2 * m] = lo16<false>(w1[m]);
+          x[8 + 2 * m + 1] = hi16<false>(w1[m]);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        const int e = e4m3_block_exp(pair_max(amax));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qf8[st][4 * hb + j] = (int)e4m3_codes4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], e);
+        sw |= (uint32_t)(127 + e) << (8 * (2 * st + hb));
+      }
+    qsw = sw >> (8 * hh);
+  }
+  if constexpr (QM == 1) {
     // A 16 x 16 block of Q is 16 rows (lanes l32 in one half of 0..31; wave
     // rows start at multiples of 32, block rows at multiples of 16) by 16
     // columns (k-step s, both half-waves): its amax takes a 5-step XOR
     // reduction over lane bits 0..3 and 5. Rows past N read as zeros, as in
     // the short last block of the quantisation kernel.
-    static_assert(!(QQ && F16), "the FP8 path takes bf16 inputs");
+    static_assert(!F16, "the FP8 paths take bf16 inputs");
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       const u32x4 w = as_u32x4(qf[s]);
@@ -211,13 +261,41 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int m = 0; m < VM; ++m) v_src_b[m] = v_src0 + 1024u * (wl + 4 * m);
 
-  auto load_k = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
-    constexpr int nl = decltype(NL)::value;
-    const auto r = rows_rsrc(Kh, j * BC, N, D * 2);
+  // QM 2: K tiles of E4M3 codes, rows padded to D + 16 bytes (the same
+  // conflict-free spread as the bf16 rows), and the tile's scale words
+  constexpr int KST8 = D + 16, KCH8 = KST8 / 16, K_INSTR8 = BC * KCH8 / 64;
+  constexpr int KM8 = (K_INSTR8 + 3) / 4;
+  const uint8_t* const K8h = reinterpret_cast<const uint8_t*>(K) + (size_t)(bh / G) * N * D;
+  const uint8_t* const Ksch = Ksc + (size_t)(bh / G) * N * 4;
+  auto k8_src = [&](int n) -> uint32_t {  // padding positions fetch chunk 0 again
+    const int i = 64 * n + lane;
+    const int kr = i / KCH8, pos = i % KCH8;
+    return (uint32_t)(kr * D + (pos < D / 16 ? pos * 16 : 0));
+  };
+  uint32_t k8_src_b[QM == 2 ? KM8 : 1];
+  if constexpr (QM == 2) {
 #pragma unroll
-    for (int m = 0; m * nl < C::K_INSTR; ++m) {
-      const int n = m * nl + w;
-      if (n < C::K_INSTR) buf_load16_lds(r, nl == 4 ? k_src_b[m] : k_src(n), t + 64 * n * 8);
+    for (int m = 0; m < KM8; ++m) k8_src_b[m] = k8_src(wl + 4 * m);
+  }
+  auto load_k = [&](auto NL, int w, int j, __bf16* t, uint32_t* sc) __attribute__((always_inline)) {
+    constexpr int nl = decltype(NL)::value;
+    if constexpr (QM == 2) {
+      const auto r = rows_rsrc(K8h, j * BC, N, D);
+#pragma unroll
+      for (int m = 0; m * nl < K_INSTR8; ++m) {
+        const int n = m * nl + w;
+        if (n < K_INSTR8)
+          buf_load16_lds(r, nl == 4 ? k8_src_b[m] : k8_src(n),
+                         reinterpret_cast<__bf16*>(reinterpret_cast<uint8_t*>(t) + 1024 * n));
+      }
+      if (w == 0) buf_load4_lds(rows_rsrc(Ksch, j * BC, N, 4), 4u * lane, sc);
+    } else {
+      const auto r = rows_rsrc(Kh, j * BC, N, D * 2);
+#pragma unroll
+      for (int m = 0; m * nl < C::K_INSTR; ++m) {
+        const int n = m * nl + w;
+        if (n < C::K_INSTR) buf_load16_lds(r, nl == 4 ? k_src_b[m] : k_src(n), t + 64 * n * 8);
+      }
     }
   };
   auto load_v = [&](auto NL, int w, int j, __bf16* t) __attribute__((always_inline)) {
@@ -301,9 +379,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // l += 1 P_t^T (if DO_PV), the product streams interleaved. Operands stream through register rings
   // two products deep (fenced so the scheduler keeps that depth instead of
   // hoisting every read, which would not fit the register budget).
-  auto mphase = [&](auto DO_S, auto DO_PV, const __bf16* kt, const __bf16* vt) __attribute__((always_inline)) {
+  auto mphase = [&](auto DO_S, auto DO_PV, const __bf16* kt, const __bf16* vt, const uint32_t* sct)
+      __attribute__((always_inline)) {
     constexpr bool do_s = decltype(DO_S)::value, do_pv = decltype(DO_PV)::value;
     constexpr int NM = (D / 16) * (BC / 32);  // = (BC / 16) * (D / 32): products per stream
+
     auto kread = [&](int i) {  // K fragment of S product i (k-step i / 2, key block i % 2)
       const int st = i / (BC / 32), kb = i % (BC / 32);
       return ld_lds16(&kt[(32 * kb + l32) * KST + 16 * st + 8 * hh]);
@@ -313,6 +393,53 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const __bf16* p = vt + vrow[b] + 16 * tk * D;  // rows 16 tk + 4 hh + tr_e: slots 8hh + 0..3
       return cat8(ld_lds_tr(p), ld_lds_tr(p + 8 * D));  // rows + 8: slots 8hh + 4..7
     };
+    if constexpr (QM == 2) {
+      // S^T on the scaled FP8 instruction: product j takes k-step j / 2 (64
+      // columns) of key block j % 2, one per four P V products; the K code
+      // operands stream through a two-deep ring, the keys' scale words (the
+      // instruction's block 2 st + hh in byte 2 st) are read once per tile
+      constexpr int NS = 2 * NST, SEV = NM / NS;
+      static_assert(NM % NS == 0, "S products interleave evenly");
+      const uint8_t* const k8 = reinterpret_cast<const uint8_t*>(kt);
+      auto kread8 = [&](int j) {
+        const uint8_t* p = k8 + (32 * (j & 1) + l32) * KST8 + 64 * (j >> 1) + 16 * hh;
+        const u32x4 a = as_u32x4(ld_lds16(reinterpret_cast<const __bf16*>(p)));
+        const u32x4 b = as_u32x4(ld_lds16(reinterpret_cast<const __bf16*>(p + 32)));
+        return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+      };
+      const uint32_t ksw[2] = {sct[l32] >> (8 * hh), sct[32 + l32] >> (8 * hh)};
+      i32x8 kr8[2] = {kread8(0), kread8(1)};
+      constexpr int R = RING;
+      bf16x8 vr[R];
+      const uint32_t one2 = 0x3F803F80u;
+      const bf16x8 ones = as_bf16x8(u32x4{one2, one2, one2, one2});
+      if constexpr (do_pv) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) vr[j] = vread(j);
+      }
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < (do_pv ? NM : NS * SEV); ++i) {
+        if (i % SEV == 0) {
+          const int j = i / SEV, st = j >> 1, kb = j & 1;
+          if (st == 0)
+            sacc[kb] = mfma_mx<0, true>(kr8[j & 1], qf8[0], sacc[kb], ksw[kb], qsw);
+          else
+            sacc[kb] = mfma_mx<2, false>(kr8[j & 1], qf8[NST - 1], sacc[kb], ksw[kb], qsw);
+          if (j + 2 < NS) kr8[j & 1] = kread8(j + 2);
+        }
+        if constexpr (do_pv) {
+          const int tk = i / (D / 32), b = i % (D / 32);
+          o[b] = mfma32x<F16>(vr[i % R], as_bf16x8(pf[tk]), o[b]);
+          if (i + R < NM) vr[i % R] = vread(i + R);
+          if (b == D / 32 - 1) lacc = mfma32x<F16>(ones, as_bf16x8(pf[tk]), lacc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
     constexpr int R = RING;
     bf16x8 kr[R], vr[R];
     const uint32_t one2 = F16 ? 0x3C003C00u : 0x3F803F80u;
@@ -374,13 +501,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // softmax(t), slot 2t+2, after the last reads of those buffers (slot 2t+1),
   // and waits for them at the end of its M(t), slot 2t+3; their first reader is
   // group A's M(t+1) in slot 2t+4.
-  load_k(eight{}, wave, 0, ks0);
-  if (T > 1) load_k(eight{}, wave, 1, ks1);
+  load_k(eight{}, wave, 0, ks0, ksc0);
+  if (T > 1) load_k(eight{}, wave, 1, ks1, ksc1);
   load_v(eight{}, wave, 0, vs0);
   wait_vmem_all();
   __syncthreads();
   if (grp == 1) __syncthreads();
-  mphase(yes{}, no{}, ks0, vs0);  // S_0
+  mphase(yes{}, no{}, ks0, vs0, ksc0);  // S_0
   slot_barrier();
   // one tile, t: buffers of parity P = t & 1 (static in each copy)
   auto tile = [&](auto P, int t) __attribute__((always_inline)) {
@@ -389,13 +516,15 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __bf16* k_next = odd ? ks0 : ks1;  // K_{t+1}
     __bf16* v_this = odd ? vs1 : vs0;  // V_t
     __bf16* v_next = odd ? vs0 : vs1;  // V_{t+1}, loaded now
+    uint32_t* sc_this = odd ? ksc1 : ksc0;  // scale words of K_t, then K_{t+2}
+    uint32_t* sc_next = odd ? ksc0 : ksc1;
     if (grp == 1) {
-      if (t + 2 < T) load_k(four{}, wl, t + 2, k_this);
+      if (t + 2 < T) load_k(four{}, wl, t + 2, k_this, sc_this);
       if (t + 1 < T) load_v(four{}, wl, t + 1, v_next);
     }
     softmax(t);
     slot_barrier();
-    mphase(yes{}, yes{}, k_next, v_this);
+    mphase(yes{}, yes{}, k_next, v_this, sc_next);
     wait_vmem_all();  // (group A has none in flight; waiting on every wave keeps the
     slot_barrier();   //  compiler's view of pending loads exact)
   };
@@ -413,10 +542,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (; t < T; ++t) {
     if (grp == 1) {
       if (t & 1) {
-        if (t + 2 < T) load_k(four{}, wl, t + 2, ks1);
+        if (t + 2 < T) load_k(four{}, wl, t + 2, ks1, ksc1);
         if (t + 1 < T) load_v(four{}, wl, t + 1, vs0);
       } else {
-        if (t + 2 < T) load_k(four{}, wl, t + 2, ks0);
+        if (t + 2 < T) load_k(four{}, wl, t + 2, ks0, ksc0);
         if (t + 1 < T) load_v(four{}, wl, t + 1, vs1);
       }
     }
@@ -445,26 +574,27 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     LSE[(size_t)bh * N + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool F16, bool QQ>
+template <int D, bool CAUSAL, bool F16, int QM>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdCfg<D>;
   const int nq = (a.N + C::BR - 1) / C::BR;
   const long long total = (long long)nq * a.B * a.H;
-  return launch_kernel(fwd_kernel<D, CAUSAL, F16, QQ>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
+  return launch_kernel(fwd_kernel<D, CAUSAL, F16, QM>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
-                       a.LSE, a.N, a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e);
+                       a.LSE, a.N, a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e, a.k_scales);
 }
 
-template <bool F16, bool QQ>
+template <bool F16, int QM>
 static hipError_t launch_fwd_dt(const FwdArgs& a) {
   if (a.d == 128)
-    return a.causal ? launch_fwd_t<128, true, F16, QQ>(a) : launch_fwd_t<128, false, F16, QQ>(a);
-  return a.causal ? launch_fwd_t<64, true, F16, QQ>(a) : launch_fwd_t<64, false, F16, QQ>(a);
+    return a.causal ? launch_fwd_t<128, true, F16, QM>(a) : launch_fwd_t<128, false, F16, QM>(a);
+  return a.causal ? launch_fwd_t<64, true, F16, QM>(a) : launch_fwd_t<64, false, F16, QM>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.quant_q) return a.f16 ? hipErrorInvalidValue : launch_fwd_dt<false, true>(a);
-  return a.f16 ? launch_fwd_dt<true, false>(a) : launch_fwd_dt<false, false>(a);
+  if (a.fp8 == 1) return a.f16 ? hipErrorInvalidValue : launch_fwd_dt<false, 1>(a);
+  if (a.fp8 == 2) return a.f16 || a.k_scales == nullptr ? hipErrorInvalidValue : launch_fwd_dt<false, 2>(a);
+  return a.f16 ? launch_fwd_dt<true, 0>(a) : launch_fwd_dt<false, 0>(a);
 }
 
 }  // namespace fa

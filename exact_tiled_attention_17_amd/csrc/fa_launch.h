@@ -19,7 +19,12 @@ struct FwdArgs {
   hipStream_t stream;
   bool f16;  // element type of Q, K, V, O: IEEE binary16 (true) or bf16
   int Hkv;   // K/V heads; divides H (query head h reads K/V head h / (H / Hkv))
-  bool quant_q = false;  // FP8 path: quantise Q to E4M3 per 16 x 16 block on load (bf16 only)
+  // FP8 paths (bf16 only): 0 none; 1: 16 x 16 blocks, Q quantised on load, K
+  // given dequantised (bf16); 2: 1 x 32 blocks, Q quantised on load, K given
+  // as E4M3 codes ([B,Hkv,N,d] bytes) with E8M0 scale bytes in k_scales
+  // ([B,Hkv,N,d/32]), the S products on the scaled FP8 matrix instruction
+  int fp8 = 0;
+  const uint8_t* k_scales = nullptr;
 };
 
 struct BwdArgs {
@@ -66,6 +71,18 @@ struct QuantArgs {
   bool f16;
 };
 
+// 1 x 32 blocks: codes [R, N, d] and E8M0 scale bytes (2^(byte - 127)),
+// scale_stride bytes per row (d / 32 of them written), both required
+struct QuantMxArgs {
+  const void* X;
+  uint8_t* codes;
+  uint8_t* scales;
+  int R, N, d;
+  hipStream_t stream;
+  bool f16;
+  int scale_stride;
+};
+
 // Enqueues `kernel` and returns the status of this launch alone (not the
 // runtime's sticky last error, which other libraries in the process may have
 // left behind).
@@ -84,6 +101,7 @@ hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_mass(const MassArgs& a);
 hipError_t launch_quant(const QuantArgs& a);
+hipError_t launch_quant_mx(const QuantMxArgs& a);
 
 // float32 row statistics of the backward: LSE in base 2, then -D, per query row
 // (padded to a multiple of 64 floats so that what follows stays 256-byte aligned).

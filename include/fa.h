@@ -69,7 +69,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad shape, bad scale or flag */
   FA_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128, or unknown fa_dtype */
   FA_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
-  FA_ERR_OUT_OF_MEMORY = 4, /* fa_bwd, fa_key_mass or fa_fwd_fp8 could not get its scratch */
+  FA_ERR_OUT_OF_MEMORY = 4, /* fa_bwd, fa_key_mass, fa_fwd_fp8 or fa_fwd_mxfp8 could not get its scratch */
   FA_ERR_TOO_LARGE = 5      /* fa_bwd_noalloc: B * H * N exceeds FA_NOALLOC_MAX_ROWS */
 } fa_status;
 
@@ -268,6 +268,44 @@ int fa_quantize_e4m3(const void* X, void* codes, float* scales, int R, int N,
 int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int H, int Hkv, int N, int d, int causal,
                float softmax_scale, void* stream);
+
+/*
+ * FP8 (E4M3) quantisation of 1 x 32 blocks: the alternative reading of the
+ * FP8 path ("GPU Performance Optimization Batch 1 - Design Spec", Item 3,
+ * Design, optional FP8 path, read with Item 2's MX block-wise quantisation:
+ * a block is one row by 32 consecutive columns, the OCP MX block size, which
+ * gfx950's scaled FP8 matrix instruction applies at twice the bf16 rate).
+ *
+ *   X       in : [R, N, d] 16-bit (dtype), R matrices (heads) of N rows
+ *   codes   out: [R, N, d] uint8 E4M3 codes, 16-byte aligned
+ *   scales  out: [R, N, d/32] uint8 E8M0 scales: byte s means 2^(s - 127)
+ *
+ * Block c of row n covers columns 32c .. 32c + 31. Its exponent e, the codes
+ * and the saturation rule are those of fa_quantize_e4m3 (smallest e with
+ * amax <= 448 * 2^e, at least -100, 0 for a zero block; nearest E4M3 value
+ * of x / 2^e, ties to even, zero as 0x00); the scale byte is 127 + e. Inputs
+ * must be finite. Allocates nothing. Errors: FA_ERR_INVALID_ARG (null or
+ * misaligned pointer, R or N < 1, R*N*d >= 2^40), FA_ERR_UNSUPPORTED (d not
+ * 64 or 128, unknown dtype).
+ */
+int fa_quantize_mx_e4m3(const void* X, void* codes, void* scales, int R, int N, int d, int dtype,
+                        void* stream);
+
+/*
+ * Forward pass of the FP8 path under the 1 x 32 block reading (see
+ * fa_quantize_mx_e4m3): Q and K are quantised per row and 32 columns, and O,
+ * LSE are exact attention on the dequantised decode(code) * 2^e values of Q
+ * and K, with V, P and O as in fa_fwd_ex. The S = Q K^T products run on the
+ * scaled 32x32x64 FP8 matrix instruction (E4M3 codes with their E8M0 block
+ * scales), the P V products on bf16 matrix cores. Arguments, layout and
+ * errors as fa_fwd_ex with dtype bf16 (no FP8 backward). Inputs must be
+ * finite. Takes B*Hkv*N*(d + 4) bytes of scratch (K's codes and a 4-byte
+ * scale word per key; Q is quantised as the forward loads it), stream-ordered
+ * like fa_bwd's; FA_ERR_OUT_OF_MEMORY if it cannot be had.
+ */
+int fa_fwd_mxfp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int B, int H, int Hkv, int N, int d, int causal,
+                 float softmax_scale, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -25,8 +25,8 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     assert header_functions() == ["fa_bwd", "fa_bwd_ex", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_ex",
-                                  "fa_fwd_fp8", "fa_key_mass", "fa_last_hip_error",
-                                  "fa_quantize_e4m3", "fa_status_string"]
+                                  "fa_fwd_fp8", "fa_fwd_mxfp8", "fa_key_mass", "fa_last_hip_error",
+                                  "fa_quantize_e4m3", "fa_quantize_mx_e4m3", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -229,6 +229,43 @@ def test_fwd_fp8_validates(kw, status):
     assert fwd8(**kw) == getattr(fa, status)
 
 
+def quant_mx(**kw):
+    a = dict(X=P, codes=P, scales=P + 1, R=2, N=16, d=128, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_quantize_mx_e4m3(a["X"], a["codes"], a["scales"], a["R"], a["N"], a["d"],
+                                  a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), "FA_ERR_INVALID_ARG"), (dict(X=P + 2), "FA_ERR_INVALID_ARG"),
+    (dict(codes=None), "FA_ERR_INVALID_ARG"), (dict(codes=P + 4), "FA_ERR_INVALID_ARG"),
+    (dict(scales=None), "FA_ERR_INVALID_ARG"),
+    (dict(R=0), "FA_ERR_INVALID_ARG"), (dict(N=0), "FA_ERR_INVALID_ARG"),
+    (dict(R=1 << 14, N=1 << 22, d=64), "FA_ERR_INVALID_ARG"),
+    (dict(d=96), "FA_ERR_UNSUPPORTED"), (dict(dtype=3), "FA_ERR_UNSUPPORTED"),
+])
+def test_quantize_mx_validates(kw, status):
+    assert quant_mx(**kw) == getattr(fa, status)
+
+
+def fwd_mx(**kw):
+    a = dict(GOOD, Q=P, K=P, V=P, O=P, LSE=P, Hkv=2, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_mxfp8(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["Hkv"],
+                           a["N"], a["d"], a["causal"], a["softmax_scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), "FA_ERR_INVALID_ARG"), (dict(K=P + 2), "FA_ERR_INVALID_ARG"),
+    (dict(V=None), "FA_ERR_INVALID_ARG"), (dict(O=P + 8), "FA_ERR_INVALID_ARG"),
+    (dict(LSE=P + 2), "FA_ERR_INVALID_ARG"), (dict(Hkv=3), "FA_ERR_INVALID_ARG"),
+    (dict(N=0), "FA_ERR_INVALID_ARG"), (dict(causal=5), "FA_ERR_INVALID_ARG"),
+    (dict(softmax_scale=-1.0), "FA_ERR_INVALID_ARG"), (dict(d=32), "FA_ERR_UNSUPPORTED"),
+])
+def test_fwd_mxfp8_validates(kw, status):
+    assert fwd_mx(**kw) == getattr(fa, status)
+
+
 def test_torch_fp8_wrappers_check_before_calling():
     import torch
     q = torch.zeros(1, 2, 4, 64, dtype=torch.float16)
@@ -236,6 +273,10 @@ def test_torch_fp8_wrappers_check_before_calling():
         fa.forward_fp8(q, q, q)
     with pytest.raises(TypeError):
         fa.quantize_e4m3(q.float())
+    with pytest.raises(TypeError):
+        fa.forward_mxfp8(q, q, q)
+    with pytest.raises(TypeError):
+        fa.quantize_mx_e4m3(q.float())
 
 
 @pytest.mark.parametrize("dtype", [fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16])

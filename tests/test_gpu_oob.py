@@ -12,7 +12,7 @@ them exactly.
 Here each input lives at the start of a larger allocation whose tail (1 MiB)
 holds NaN bit patterns. A read past a head's rows into the tail would carry a
 NaN through a product (0 x NaN is NaN) into the outputs. Every output of
-fa_fwd, fa_bwd, fa_key_mass and fa_fwd_fp8 must be finite and within the
+fa_fwd, fa_bwd, fa_key_mass, fa_fwd_fp8 and fa_fwd_mxfp8 must be finite and within the
 oracle bars. With one K/V head the last query heads share it, so K and V end
 at the tail too.
 """
@@ -81,9 +81,10 @@ def test_nan_tails_stay_out(fa, B, H, Hkv, N, d, causal):
     dq, dk, dv = fa.backward(do, q, k, v, o_t, lse_t, causal, scale)
     mass = fa.key_mass(q, k, lse_t, causal, scale)
     o8, lse8 = fa.forward_fp8(q, k, v, causal, scale)
+    om, lsem = fa.forward_mxfp8(q, k, v, causal, scale)
     torch.cuda.synchronize()
     for name, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv), ("mass", mass),
-                    ("O fp8", o8), ("LSE fp8", lse8)):
+                    ("O fp8", o8), ("LSE fp8", lse8), ("O mxfp8", om), ("LSE mxfp8", lsem)):
         _finite(name, t)
 
     f = {n: oracle.bf16_bits_to_f64(b) for n, b in x.items()}
@@ -98,3 +99,6 @@ def test_nan_tails_stay_out(fa, B, H, Hkv, N, d, causal):
     o8_ref, lse8_ref = oracle.fp8_attention_forward(f["q"], f["k"], f["v"], causal, scale)
     assert max_abs(to_f64(o8), o8_ref) <= O_ATOL
     assert max_abs(to_f64(lse8), lse8_ref) <= LSE_ATOL
+    om_ref, lsem_ref = oracle.mx_fp8_attention_forward(f["q"], f["k"], f["v"], causal, scale)
+    assert max_abs(to_f64(om), om_ref) <= O_ATOL
+    assert max_abs(to_f64(lsem), lsem_ref) <= LSE_ATOL
