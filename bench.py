@@ -37,6 +37,9 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_17_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_4x64x4096x128_causal.json")
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
+# S = Q K^T on FP8, P V on bf16, equal FLOPs
+PEAK_MX_MIX_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 # Page 4 ("RTX Flash Attention Implementation COMPLETE", Performance
@@ -357,20 +360,25 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         mass_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
-    # the FP8 forward (Q, K quantised per 16 x 16 block), bf16 inputs only
-    fp8_ms = None
+    # the FP8 forwards (Q, K quantised per 16 x 16 block, or per 1 x 32 block), bf16 only
+    fp8_ms = mx_ms = None
     if args.dtype == "bf16":
         o8 = torch.empty_like(q)
         l8 = torch.empty_like(lse)
-        fa.forward_fp8(q, k, v, causal, w.scale, out=o8, lse=l8)
-        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for e0, e1 in fev:
-            e0.record(stream)
-            fa.forward_fp8(q, k, v, causal, w.scale, out=o8, lse=l8)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        fp8_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
+
+        def time_fwd8(fn):
+            fn(q, k, v, causal, w.scale, out=o8, lse=l8)
+            fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for e0, e1 in fev:
+                e0.record(stream)
+                fn(q, k, v, causal, w.scale, out=o8, lse=l8)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
+
+        fp8_ms = time_fwd8(fa.forward_fp8)
+        mx_ms = time_fwd8(fa.forward_mxfp8)
         del o8, l8
 
     f_fwd, f_bwd = flops(w, causal)
@@ -404,6 +412,16 @@ def main():
     # its products run on bf16 matrix cores (the dequantised operands are exact in bf16)
     r_fp8 = roof("fa_fwd_fp8", "quant_e4m3_kernel (K) + fwd_kernel (Q quantised on load)", f_fwd, fp8_ms) \
         if fp8_ms is not None else None
+    # half its FLOPs (S = Q K^T) run on the FP8 matrix instruction (5.0 PFLOP/s dense), half
+    # (P V) on bf16 (2.5): the peak of that mix is 1 / (0.5 / 5.0 + 0.5 / 2.5) PFLOP/s
+    r_mx = None
+    if mx_ms is not None:
+        r_mx = roof("fa_fwd_mxfp8", "quant_mx_kernel (K) + fwd_kernel (S on the scaled FP8 "
+                    "instruction)", f_fwd, mx_ms)
+        r_mx["peak"] = PEAK_MX_MIX_TFLOPS
+        r_mx["frac"] = round(r_mx["achieved"] / PEAK_MX_MIX_TFLOPS, 4)
+        r_mx["peak_note"] = ("S = Q K^T at the dense FP8 peak (5000 TFLOP/s), P V at the bf16 "
+                             "peak (2500): equal FLOPs, so 1 / (0.5 / 5000 + 0.5 / 2500)")
 
     out = {
         "metric": "bf16 attention TFLOP/s fwd & fwd+bwd at 4x64x4096x128 causal, % MFMA peak",
@@ -435,6 +453,7 @@ def main():
         "roofline_fwd": r_fwd,
         "roofline_key_mass": r_mass,
         "roofline_fwd_fp8": r_fp8,
+        "roofline_fwd_mxfp8": r_mx,
         "cpu_baseline": None,
     }
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
