@@ -263,7 +263,8 @@ int fa_quantize_e4m3(const void* X, void* codes, float* scales, int R, int N,
  * gfx950's only FP8 matrix instruction faster than bf16 (the 32x32x64 one,
  * about twice the rate) scales per 32 values along the contraction, which a
  * 16-wide block cannot use without re-encoding its codes; the 16-deep FP8
- * instruction runs at the bf16 rate.
+ * instruction runs at the bf16 rate. fa_fwd_mxfp8 (1 x 32 blocks) is the FP8
+ * forward that uses the faster instruction.
  */
 int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int H, int Hkv, int N, int d, int causal,
