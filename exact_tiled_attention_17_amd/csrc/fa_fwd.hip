@@ -99,7 +99,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O,
                 float* __restrict__ LSE, int N, int BH, int G, float c_log2,
-                const uint8_t* __restrict__ Ksc) {
+                const uint8_t* __restrict__ Ksc, int pairs) {
   // BH query heads; query head bh reads K/V head bh / G (G query heads per
   // K/V head: 1 for multi-head attention, H for multi-query attention)
   using C = FwdCfg<D>;
@@ -125,10 +125,16 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) uint32_t ksc0[QM == 2 ? BC : 1];
   __shared__ __attribute__((aligned(16))) uint32_t ksc1[QM == 2 ? BC : 1];
 
+  // With `pairs` (causal only) the workgroup runs query tile nq - 1 - w and
+  // then tile w: every pair has the same number of key tiles, so the
+  // workgroups are equally long (uneven ones leave CUs idle while work is
+  // still queued) and there are half as many.
   const int nq = (N + BR - 1) / BR;
-  int bh, qt;
-  xcd_remap(blockIdx.x, nq * BH, nq, bh, qt);
-  if (CAUSAL) qt = nq - 1 - qt;  // longest rows first
+  const int nwq = pairs ? (nq + 1) / 2 : nq;
+  int bh, wq;
+  xcd_remap(blockIdx.x, nwq * BH, nwq, bh, wq);
+  const int qt_first = CAUSAL ? nq - 1 - wq : wq;  // longest rows first
+  const int nit = pairs && wq != nq - 1 - wq ? 2 : 1;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -153,6 +159,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const __bf16* const Kh = K + kvhead;
   const __bf16* const Vh = V + kvhead;
 
+  // one query tile: its sweep over the key tiles and its epilogue
+  auto run_item = [&](const int qt) __attribute__((always_inline)) {
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * rblk;  // first query row of this wave
   const int row = wrow0 + l32;       // this lane's query row
@@ -572,16 +580,25 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   if (LSE != nullptr && hh == 0)
     LSE[(size_t)bh * N + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  };
+  if constexpr (CAUSAL) {
+    for (int it = 0; it < nit; ++it) run_item(it == 0 ? qt_first : wq);
+  } else {
+    run_item(qt_first);
+  }
 }
 
 template <int D, bool CAUSAL, bool F16, int QM>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdCfg<D>;
   const int nq = (a.N + C::BR - 1) / C::BR;
-  const long long total = (long long)nq * a.B * a.H;
+  // causal: pair query tiles while that leaves at least one workgroup per CU
+  const long long heads = (long long)a.B * a.H;
+  const int pairs = CAUSAL && nq >= 2 && heads * ((nq + 1) / 2) >= kFwdPairMinWorkgroups ? 1 : 0;
+  const long long total = (pairs ? (nq + 1) / 2 : nq) * heads;
   return launch_kernel(fwd_kernel<D, CAUSAL, F16, QM>, dim3((unsigned)total), dim3(C::THREADS), a.stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
-                       a.LSE, a.N, a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e, a.k_scales);
+                       a.LSE, a.N, a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e, a.k_scales, pairs);
 }
 
 template <bool F16, int QM>

@@ -115,6 +115,10 @@ inline size_t rowstat_floats(int B, int H, int N) {
 // attention: B * ceil(N / 128) workgroups), so the group is split until the
 // grid has 1024 workgroups (four per compute unit), each split writing
 // float32 partial sums (8 * S * B * Hkv * N * d bytes in all, kept under 1 GiB).
+// The causal forward and dQ pass pair query tiles (tile nq - 1 - w with tile
+// w in one workgroup) when at least this many workgroups remain.
+constexpr long long kFwdPairMinWorkgroups = 256;
+
 // The dK/dV pass can give a workgroup pairs of key blocks (block p with
 // block nkb - 1 - p: equally long workgroups under the causal mask, fewer of
 // them). Pairs per workgroup: the largest of 4, 2, 1 that leaves at least

@@ -1,6 +1,9 @@
-"""GPU parity for the dK/dV pass when it gives each workgroup two key blocks.
+"""GPU parity for the kernels that give each workgroup a pair of tiles.
 
-When the pairs of key blocks (block p with block nkb - 1 - p; the middle
+The causal forward (and dQ pass) pair query tile nq - 1 - w with tile w in
+one workgroup when that leaves at least 256 workgroups: the workgroup runs
+the two tiles' sweeps one after the other, and every pair has the same
+number of key tiles. When the pairs of key blocks (block p with block nkb - 1 - p; the middle
 block of an odd count alone) number at least 1024 over all heads, the dK/dV
 pass gives each workgroup one or more pairs and runs its step pipeline from
 one block straight into the next: it loads the next block's K or V rows in
@@ -49,12 +52,12 @@ def _grad_err(mine, ref):
 
 
 @pytest.mark.parametrize("B,H,Hkv,N,d,causal", CASES)
-def test_paired_key_blocks(fa, B, H, Hkv, N, d, causal):
+def test_paired_tiles(fa, B, H, Hkv, N, d, causal):
     import torch
     nkb = (N + 127) // 128
     assert B * Hkv * ((nkb + 1) // 2) >= 1024  # the shapes must take the paired path
     seed = 7700 + N + 3 * H + Hkv + d + int(causal)
-    announce(f"dkdv pairs B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} seed={seed}")
+    announce(f"pairs B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} seed={seed}")
     x = ai.make_qkv(B, H, N, d, seed, with_do=True, Hkv=Hkv)
     scale = float(np.float32(1.0 / math.sqrt(d)))
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
