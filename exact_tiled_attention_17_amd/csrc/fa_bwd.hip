@@ -556,7 +556,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const __bf16* __restrict__ O, const float* __restrict__ LSE,
                    float* __restrict__ rowstat, __bf16* __restrict__ dQ, int N, int BH,
-                   int G, float c_log2, float scale) {
+                   int G, float c_log2, float scale, int pairs) {
   // BH query heads; query head bh reads K/V head bh / G
   using C = DqCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, CH = C::CH, TI = C::TI;
@@ -570,10 +570,14 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) __bf16 vs0[BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 vs1[BC * D];
 
+  // With `pairs` (causal only) the workgroup runs query tile nq - 1 - w and
+  // then tile w, as the forward does: equally long workgroups, half as many.
   const int nq = (N + BR - 1) / BR;
-  int bh, qt;
-  xcd_remap(blockIdx.x, nq * BH, nq, bh, qt);
-  if (CAUSAL) qt = nq - 1 - qt;  // longest rows first
+  const int nwq = pairs ? (nq + 1) / 2 : nq;
+  int bh, wq;
+  xcd_remap(blockIdx.x, nwq * BH, nwq, bh, wq);
+  const int qt_first = CAUSAL ? nq - 1 - wq : wq;  // longest rows first
+  const int nit = pairs && wq != nq - 1 - wq ? 2 : 1;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -597,6 +601,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const auto rO = make_rsrc(O + head, head_bytes);
   const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
 
+  // one query tile: its row statistics, its sweep over the key tiles, its dQ
+  auto run_item = [&](const int qt) __attribute__((always_inline)) {
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * rblk;
   const int row = wrow0 + l32;
@@ -859,6 +865,12 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       w[1] = pack2<F16>(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
       st_global8(Drow + 32 * b + 8 * g + 4 * hh, w);
     }
+  };
+  if constexpr (CAUSAL) {
+    for (int it = 0; it < nit; ++it) run_item(it == 0 ? qt_first : wq);
+  } else {
+    run_item(qt_first);
+  }
 }
 
 template <int D, bool CAUSAL, bool F16>
@@ -870,12 +882,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   {
     // dQ pass first: it also writes the row statistics the dK/dV pass reads
     const int nq = (a.N + Cq::BR - 1) / Cq::BR;
-    const long long total = (long long)nq * a.B * a.H;
+    const long long heads = (long long)a.B * a.H;
+    const int pairs = CAUSAL && nq >= 2 && heads * ((nq + 1) / 2) >= kFwdPairMinWorkgroups ? 1 : 0;
+    const long long total = (pairs ? (nq + 1) / 2 : nq) * heads;
     const hipError_t e = launch_kernel(
         bwd_dq_kernel<D, CAUSAL, F16>, dim3((unsigned)total), dim3(Cq::THREADS), a.stream,
         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO,
         (const __bf16*)a.O, a.LSE, rowstat, (__bf16*)a.dQ, a.N, a.B * a.H, a.H / a.Hkv, c_log2,
-        a.softmax_scale);
+        a.softmax_scale, pairs);
     if (e != hipSuccess) return e;
   }
   {
