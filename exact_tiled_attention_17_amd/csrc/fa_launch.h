@@ -119,6 +119,10 @@ inline size_t rowstat_floats(int B, int H, int N) {
 // w in one workgroup) when at least this many workgroups remain.
 constexpr long long kFwdPairMinWorkgroups = 256;
 
+// The causal key-mass pass pairs key blocks when at least this many
+// workgroups (four per CU run at once) remain.
+constexpr long long kMassPairMinWorkgroups = 1024;
+
 // The dK/dV pass can give a workgroup pairs of key blocks (block p with
 // block nkb - 1 - p: equally long workgroups under the causal mask, fewer of
 // them). Pairs per workgroup: the largest of 4, 2, 1 that leaves at least

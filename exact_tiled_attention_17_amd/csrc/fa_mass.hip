@@ -36,7 +36,7 @@ template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const float* __restrict__ LSE, float* __restrict__ part, int N, int BH, int G,
-                     float c_log2) {
+                     float c_log2, int pairs) {
   // BH query heads; query head bh reads K head bh / G
   using C = MassCfg<D>;
   constexpr int BRB = C::BRB, QB = C::QB, CH = C::CH, LM = C::TI / C::NW;
@@ -48,9 +48,13 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) float ls0[BRB];  // LSE (natural log) of the step's queries
   __shared__ __attribute__((aligned(16))) float ls1[BRB];
 
+  // With `pairs` (causal only) the workgroup runs key block w, then block
+  // nkb - 1 - w: every pair has the same number of query steps.
   const int nkb = (N + C::BCB - 1) / C::BCB;
-  int bh, kb;
-  xcd_remap(blockIdx.x, nkb * BH, nkb, bh, kb);
+  const int nwb = pairs ? (nkb + 1) / 2 : nkb;
+  int bh, wb;
+  xcd_remap(blockIdx.x, nwb * BH, nwb, bh, wb);
+  const int nit = pairs && wb != nkb - 1 - wb ? 2 : 1;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -62,15 +66,6 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const __bf16* const Qh = Q + (size_t)bh * N * D;
   const float* const Lh = LSE + (size_t)bh * N;
   const auto rK = make_rsrc(K + (size_t)(bh / G) * N * D, head_bytes);
-
-  const int k0 = kb * C::BCB;
-  const int kw0 = k0 + 32 * wave;  // this wave's first key
-  const int key = kw0 + l32;       // this lane's key (column of S); rows past N read as 0
-
-  bf16x8 frag[D / 16];  // the lane's K row as B operands
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    frag[s] = as_bf16x8(buf_load16(rK, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
 
   // ---- step loads, straight from HBM into LDS: instruction n fills chunk
   // positions [64 n, 64 n + 64) of the Q tile (dealt round-robin over the
@@ -85,6 +80,25 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     src_w[m] = (uint32_t)(r * (D * 2) + ((pc ^ swz<D>(r)) * 16));
   }
   const int nqt = (N + BRB - 1) / BRB;
+  int rw = tile_off<D>(l32, 8 * hh);  // operand row l32, chunk hh; k-step st at rw ^ 16 st
+  asm volatile("" : "+v"(rw));
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // one key block: its sweep over the query steps and its column sums
+  auto run_item = [&](const int kb) __attribute__((always_inline)) {
+  const int k0 = kb * C::BCB;
+  const int kw0 = k0 + 32 * wave;  // this wave's first key
+  const int key = kw0 + l32;       // this lane's key (column of S); rows past N read as 0
+
+  bf16x8 frag[D / 16];  // the lane's K row as B operands
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    frag[s] = as_bf16x8(buf_load16(rK, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
+
   const int i0 = CAUSAL ? k0 / BRB : 0;  // first query tile that sees the block's keys
   const int nsteps = nqt - i0;
   auto load_step = [&](int s, __bf16* qd, float* ld) __attribute__((always_inline)) {
@@ -94,9 +108,6 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int m = 0; m < LM; ++m) buf_load16_lds(rQ, src_w[m], qd + 64 * (wave + C::NW * m) * 8);
     if (wave == 0) buf_load4_lds(rows_rsrc(Lh, q0, N, 4), 4u * lane, ld);
   };
-
-  int rw = tile_off<D>(l32, 8 * hh);  // operand row l32, chunk hh; k-step st at rw ^ 16 st
-  asm volatile("" : "+v"(rw));
 
   float colsum = 0.f;  // this lane's share of its key's mass (half the rows of each block)
   auto step = [&](int s, const __bf16* tile, const float* lse) __attribute__((always_inline)) {
@@ -140,12 +151,7 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         colsum += (p[0] + p[1]) + (p[2] + p[3]);
       }
   };
-  auto barrier = [] {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
+  barrier();  // the previous block's last step is read by every wave
   load_step(0, qs0, ls0);
   wait_vmem_all();
   barrier();
@@ -165,6 +171,12 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // the two half-waves hold the other rows of the same keys
   colsum += __shfl_xor(colsum, 32);
   if (hh == 0 && key < N) part[(size_t)bh * N + key] = colsum;
+  };
+  if constexpr (CAUSAL) {
+    for (int it = 0; it < nit; ++it) run_item(it == 0 ? wb : nkb - 1 - wb);
+  } else {
+    run_item(wb);
+  }
 }
 
 // mass[b, j] = sum_h part[b, h, j], heads added in order 0 .. H-1
@@ -185,10 +197,12 @@ template <int D, bool CAUSAL, bool F16>
 static hipError_t launch_mass_t(const MassArgs& a) {
   using C = MassCfg<D>;
   const int nkb = (a.N + C::BCB - 1) / C::BCB;
-  const long long grid = (long long)nkb * a.B * a.H;
+  const long long heads = (long long)a.B * a.H;
+  const int pairs = CAUSAL && nkb >= 2 && heads * ((nkb + 1) / 2) >= kMassPairMinWorkgroups ? 1 : 0;
+  const long long grid = (pairs ? (nkb + 1) / 2 : nkb) * heads;
   hipError_t e = launch_kernel(key_mass_kernel<D, CAUSAL, F16>, dim3((unsigned)grid), dim3(C::THREADS),
                                a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, a.LSE, a.part, a.N,
-                               a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e);
+                               a.B * a.H, a.H / a.Hkv, a.softmax_scale * kLog2e, pairs);
   if (e != hipSuccess) return e;
   const long long total = (long long)a.B * a.N;
   return launch_kernel(key_mass_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),

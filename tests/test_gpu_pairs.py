@@ -97,3 +97,35 @@ def test_paired_tiles(fa, B, H, Hkv, N, d, causal):
         for name, got, ref in (("dk", dk, dk_ref), ("dv", dv, dv_ref)):
             err = _grad_err(to_f64(got[b, j]), ref)
             assert err <= GRAD_RTOL, (name, b, j, err)
+
+
+MASS_CASES = [  # B, H, Hkv, N, d   (causal; key-block pairs = B * H * ceil(nkb / 2) >= 1024)
+    (1, 128, 128, 2048, 128),   # 16 key blocks per head
+    (1, 136, 136, 1920, 64),    # 15: the middle block alone, d = 64
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d", MASS_CASES)
+def test_paired_key_mass(fa, B, H, Hkv, N, d):
+    """The causal key-mass pass pairs key block w with block nkb - 1 - w in one
+    workgroup ("GPU Performance Optimization Batch 1 - Design Spec", Item 4,
+    Design: the mass each key receives, summed over rows and heads). With the
+    oracle's LSE as input, every key's mass must match the oracle's, and no
+    element may stay as the NaN the output was filled with."""
+    import torch
+    nkb = (N + 127) // 128
+    assert B * H * ((nkb + 1) // 2) >= 1024  # the shape must take the paired path
+    seed = 7900 + N + H + d
+    announce(f"pairs key mass B={B} H={H} N={N} d={d} seed={seed}")
+    x = ai.make_qkv(B, H, N, d, seed, Hkv=Hkv)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    f = {n: oracle.bf16_bits_to_f64(b) for n, b in x.items()}
+    ref = oracle.key_mass(f["q"], f["k"], True, scale)
+    _, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], True, scale)
+    q, k = to_dev(x["q"]), to_dev(x["k"])
+    out = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.key_mass(q, k, torch.from_numpy(lse_ref.astype(np.float32)).cuda(), True, scale, out=out)
+    torch.cuda.synchronize()
+    m = to_f64(out)
+    assert np.isfinite(m).all()
+    assert max_abs(m, ref) / np.max(np.abs(ref)) <= 1e-3
