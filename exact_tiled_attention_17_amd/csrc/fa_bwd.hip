@@ -854,6 +854,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (grp == 0) slot_barrier();
 
   // ---- epilogue: dQ = scale * dQ^T, bf16 ---------------------------------------
+  // (direct 8-byte stores: staging through LDS, as the forward does, made
+  // this kernel spill inside its tile loop)
   if (!wave_active || row >= N) return;
   __bf16* Drow = dQ + head + (size_t)row * D;
 #pragma unroll

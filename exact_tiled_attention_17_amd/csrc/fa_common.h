@@ -231,6 +231,40 @@ __device__ __forceinline__ void st_lds8(__bf16* p, u32x2 v) {
   *reinterpret_cast<u32x2*>(p) = v;
 }
 
+// Writes a wave's 32 x D tile, held transposed in D / 32 accumulators (lane
+// l: row l % 32; register r of block b: column 32 b + 8 (r / 4) + 4 (l / 32)
+// + r % 4), each row scaled by the lane's `mul` and rounded to the 16-bit
+// type, to rows row0 .. row0 + 31 of a row-major [*, D] tensor `dst` (rows
+// >= nrows are skipped). The tile goes through `stage`, 32 * D elements of
+// LDS owned by this wave, so that each global store instruction writes
+// 64 x 16 consecutive bytes (whole rows) instead of 64 scattered 8-byte
+// pieces. In `stage`, 16-byte chunk c of row r sits at c ^ (r mod CPR), CPR
+// the chunks per row, which spreads both the writes and the reads over the
+// banks. Every lane of the wave must run it (rows past the end included).
+template <int D, bool F16>
+__device__ __forceinline__ void store_rows_via_lds(const f32x16 (&acc)[D / 32], float mul, __bf16* stage,
+                                                   __bf16* dst, int row0, int nrows) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;    // rows per store instruction
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack2<F16>(acc[b][4 * g] * mul, acc[b][4 * g + 1] * mul);
+      w[1] = pack2<F16>(acc[b][4 * g + 2] * mul, acc[b][4 * g + 3] * mul);
+      const int c = (4 * b + g) ^ (l32 & (CPR - 1));
+      st_lds8(stage + l32 * D + 8 * c + 4 * hh, w);
+    }
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = k * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * D + 8 * (c ^ (r & (CPR - 1))));
+    if (row0 + r < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)(row0 + r) * D + 8 * c) = v;
+  }
+}
+
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,

@@ -509,6 +509,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // softmax(t), slot 2t+2, after the last reads of those buffers (slot 2t+1),
   // and waits for them at the end of its M(t), slot 2t+3; their first reader is
   // group A's M(t+1) in slot 2t+4.
+  __syncthreads();  // a previous tile's epilogue may still read its O stage in these buffers
   load_k(eight{}, wave, 0, ks0, ksc0);
   if (T > 1) load_k(eight{}, wave, 1, ks1, ksc1);
   load_v(eight{}, wave, 0, vs0);
@@ -564,21 +565,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (grp == 0) slot_barrier();
 
   // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l) ------------------------
+  // O goes out through an 8 KB LDS stage per wave in the (now idle) K/V tile
+  // buffers; the next tile's loads wait for a barrier first
   if (!wave_active) return;
   const float l_tot = lacc[0];
-  if (row >= N) return;
-  const float inv = 1.f / l_tot;
-  __bf16* Orow = O + head + (size_t)row * D;
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = pack2<F16>(o[b][4 * g] * inv, o[b][4 * g + 1] * inv);
-      w[1] = pack2<F16>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
-      st_global8(Orow + 32 * b + 8 * g + 4 * hh, w);
-    }
-  if (LSE != nullptr && hh == 0)
+  __bf16* const stage = (wave < 2 ? ks0 : wave < 4 ? ks1 : wave < 6 ? vs0 : vs1) + (wave & 1) * 32 * D;
+  store_rows_via_lds<D, F16>(o, 1.f / l_tot, stage, O + head, wrow0, N);
+  if (LSE != nullptr && hh == 0 && row < N)
     LSE[(size_t)bh * N + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   };
   if constexpr (CAUSAL) {
