@@ -806,6 +806,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // resource (rows_rsrc) and fills its buffer with zeros without reading memory.
   const int T4 = (T + 3) & ~3;
   const int jw4 = (jw_last + 4) & ~3;
+  __syncthreads();  // a previous tile's epilogue may still read its dQ stage in these buffers
   load_tile(eight{}, Kh, wave, 0, ks0);
   load_tile(eight{}, Vh, wave, 0, vs0);
   load_tile(eight{}, Kh, wave, 1, ks1);
@@ -853,20 +854,11 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
   if (grp == 0) slot_barrier();
 
-  // ---- epilogue: dQ = scale * dQ^T, bf16 ---------------------------------------
-  // (direct 8-byte stores: staging through LDS, as the forward does, made
-  // this kernel spill inside its tile loop)
-  if (!wave_active || row >= N) return;
-  __bf16* Drow = dQ + head + (size_t)row * D;
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = pack2<F16>(acc[b][4 * g] * scale, acc[b][4 * g + 1] * scale);
-      w[1] = pack2<F16>(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
-      st_global8(Drow + 32 * b + 8 * g + 4 * hh, w);
-    }
+  // ---- epilogue: dQ = scale * dQ^T, bf16, through an 8 KB LDS stage per wave
+  // in the (now idle) K tile buffers; the next tile's loads wait for a barrier
+  if (!wave_active) return;
+  __bf16* const stage = (wave < 2 ? ks0 : wave < 4 ? ks1 : wave < 6 ? ks2 : ks3) + (wave & 1) * 32 * D;
+  store_rows_via_lds<D, F16>(acc, scale, stage, dQ + head, wrow0, N);
   };
   if constexpr (CAUSAL) {
     for (int it = 0; it < nit; ++it) run_item(it == 0 ? qt_first : wq);

@@ -246,7 +246,11 @@ __device__ __forceinline__ void store_rows_via_lds(const f32x16 (&acc)[D / 32], 
                                                    __bf16* dst, int row0, int nrows) {
   constexpr int CPR = D / 8;       // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;    // rows per store instruction
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  // (the lane index is made opaque so that the addresses below are formed
+  // here, not hoisted out of the caller's loops and kept live across them)
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
