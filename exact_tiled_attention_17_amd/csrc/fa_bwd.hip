@@ -603,262 +603,262 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // one query tile: its row statistics, its sweep over the key tiles, its dQ
   auto run_item = [&](const int qt) __attribute__((always_inline)) {
-  const int q0 = qt * BR;
-  const int wrow0 = q0 + 32 * rblk;
-  const int row = wrow0 + l32;
-  const int nkv_all = (N + BC - 1) / BC;
-  const int last_row_wg = min(q0 + BR, N) - 1;
-  const int T = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;  // key tiles
-  const bool wave_active = wrow0 < N;
-  // last key tile this wave needs (-1: none)
-  const int jw_last = !wave_active ? -1 : CAUSAL ? min(wrow0 + 31, N - 1) / BC : T - 1;
+    const int q0 = qt * BR;
+    const int wrow0 = q0 + 32 * rblk;
+    const int row = wrow0 + l32;
+    const int nkv_all = (N + BC - 1) / BC;
+    const int last_row_wg = min(q0 + BR, N) - 1;
+    const int T = CAUSAL ? min(nkv_all, last_row_wg / BC + 1) : nkv_all;  // key tiles
+    const bool wave_active = wrow0 < N;
+    // last key tile this wave needs (-1: none)
+    const int jw_last = !wave_active ? -1 : CAUSAL ? min(wrow0 + 31, N - 1) / BC : T - 1;
 
-  // Q^T and dO^T operands (rows past N read as zeros), and the row statistics:
-  // the LSE in base 2, and D = dO . O (the lane's half of the row, then its
-  // partner's). This pass runs first and stores both for the dK/dV pass.
-  bf16x8 qf[D / 16], of[D / 16];
-  float dacc = 0.f;
+    // Q^T and dO^T operands (rows past N read as zeros), and the row statistics:
+    // the LSE in base 2, and D = dO . O (the lane's half of the row, then its
+    // partner's). This pass runs first and stores both for the dK/dV pass.
+    bf16x8 qf[D / 16], of[D / 16];
+    float dacc = 0.f;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const uint32_t off = (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2;
-    qf[s] = as_bf16x8(buf_load16(rQ, off));
-    of[s] = as_bf16x8(buf_load16(rdO, off));
-    const u32x4 ow = buf_load16(rO, off), dw = as_u32x4(of[s]);
+    for (int s = 0; s < D / 16; ++s) {
+      const uint32_t off = (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2;
+      qf[s] = as_bf16x8(buf_load16(rQ, off));
+      of[s] = as_bf16x8(buf_load16(rdO, off));
+      const u32x4 ow = buf_load16(rO, off), dw = as_u32x4(of[s]);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      dacc += lo16<F16>(ow[m]) * lo16<F16>(dw[m]);
-      dacc += hi16<F16>(ow[m]) * hi16<F16>(dw[m]);
+      for (int m = 0; m < 4; ++m) {
+        dacc += lo16<F16>(ow[m]) * lo16<F16>(dw[m]);
+        dacc += hi16<F16>(ow[m]) * hi16<F16>(dw[m]);
+      }
     }
-  }
-  const float dval = pair_sum(dacc);
-  f32x16 negd16;
+    const float dval = pair_sum(dacc);
+    f32x16 negd16;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) negd16[r] = -dval;
-  const float l2 =
-      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, (uint32_t)row * 4u, 0, 0)) * kLog2e;
-  const float neg_l2 = -l2;
-  if (hh == 0 && row < N) {
-    rowstat[(size_t)bh * N + row] = l2;                     // LSE in base 2
-    rowstat[(size_t)BH * N + (size_t)bh * N + row] = -dval; // -D
-  }
-
-  // ---- tile loads, straight from HBM into LDS: instruction n of a tile fills
-  // chunk positions [64 n, 64 n + 64); each lane fetches the chunk the layout
-  // puts at its position. K and V tiles share the layout, hence the offsets.
-  auto src = [&](int n) -> uint32_t {
-    const int p = 64 * n + lane;
-    const int r = p / CH, pc = p % CH;
-    return (uint32_t)(r * (D * 2) + ((pc ^ swz<D>(r)) * 16));
-  };
-  constexpr int LM = (TI + 3) / 4;
-  uint32_t src_b[LM];  // this wave's offsets as one of the four in-loop loaders
-#pragma unroll
-  for (int m = 0; m < LM; ++m) src_b[m] = src(wl + 4 * m);
-  // tile j of K or V (src = the head's first row), through a resource that
-  // starts at the tile's first key and ends at key N
-  auto load_tile = [&](auto NL, const __bf16* src_head, int w, int j, __bf16* t)
-      __attribute__((always_inline)) {
-    constexpr int nl = decltype(NL)::value;
-    const auto r = rows_rsrc(src_head, j * BC, N, D * 2);
-#pragma unroll
-    for (int m = 0; m * nl < TI; ++m) {
-      const int n = m * nl + w;
-      if (n < TI) buf_load16_lds(r, nl == 4 ? src_b[m] : src(n), t + 64 * n * 8);
+    for (int r = 0; r < 16; ++r) negd16[r] = -dval;
+    const float l2 =
+        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, (uint32_t)row * 4u, 0, 0)) * kLog2e;
+    const float neg_l2 = -l2;
+    if (hh == 0 && row < N) {
+      rowstat[(size_t)bh * N + row] = l2;                     // LSE in base 2
+      rowstat[(size_t)BH * N + (size_t)bh * N + row] = -dval; // -D
     }
-  };
-  using four = std::integral_constant<int, 4>;
-  using eight = std::integral_constant<int, 8>;
 
-  // ---- LDS read offsets (elements) -----------------------------------------------
-  // With the swizzle, the operand-row read of k-step st (row 32 kb + l32, chunk
-  // 2 st + hh) sits at rw ^ 16 st (+ 32 kb D), and the transposing read of d
-  // block b (rows 16 t + 4 hh + tr_e, and + 8; column 32 b + tr_col) at
-  // tw ^ 32 b (+ 16 t D): one register each, one XOR per read.
-  int rw = tile_off<D>(l32, 8 * hh);
-  int tw0 = tile_off<D>(4 * hh + tr_e, tr_col);
-  int tw1 = tile_off<D>(4 * hh + tr_e + 8, tr_col);
-  asm volatile("" : "+v"(rw), "+v"(tw0), "+v"(tw1));
-
-  // ---- running state -----------------------------------------------------------
-  f32x16 acc[D / 32];  // dQ^T: M = d, N = this wave's 32 queries
+    // ---- tile loads, straight from HBM into LDS: instruction n of a tile fills
+    // chunk positions [64 n, 64 n + 64); each lane fetches the chunk the layout
+    // puts at its position. K and V tiles share the layout, hence the offsets.
+    auto src = [&](int n) -> uint32_t {
+      const int p = 64 * n + lane;
+      const int r = p / CH, pc = p % CH;
+      return (uint32_t)(r * (D * 2) + ((pc ^ swz<D>(r)) * 16));
+    };
+    constexpr int LM = (TI + 3) / 4;
+    uint32_t src_b[LM];  // this wave's offsets as one of the four in-loop loaders
 #pragma unroll
-  for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
-  f32x16 s[BC / 32], dp[BC / 32];  // S^T, dP^T of the tile in flight
-  u32x4 dsf[BC / 16];              // dS^T as B operands, 4 k-steps of 16 keys
+    for (int m = 0; m < LM; ++m) src_b[m] = src(wl + 4 * m);
+    // tile j of K or V (src = the head's first row), through a resource that
+    // starts at the tile's first key and ends at key N
+    auto load_tile = [&](auto NL, const __bf16* src_head, int w, int j, __bf16* t)
+        __attribute__((always_inline)) {
+      constexpr int nl = decltype(NL)::value;
+      const auto r = rows_rsrc(src_head, j * BC, N, D * 2);
+#pragma unroll
+      for (int m = 0; m * nl < TI; ++m) {
+        const int n = m * nl + w;
+        if (n < TI) buf_load16_lds(r, nl == 4 ? src_b[m] : src(n), t + 64 * n * 8);
+      }
+    };
+    using four = std::integral_constant<int, 4>;
+    using eight = std::integral_constant<int, 8>;
 
-  // V(u): dS^T of key tile u from s, dp (= dP^T - D)
-  auto vphase = [&](int u) __attribute__((always_inline)) {
-    const int kv0 = u * BC;
-    const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
-    if (need_mask) {
-      // Key kv0 + 32 kb + 8 (r / 4) + 4 hh + r % 4 is masked iff its offset
-      // 32 kb + 8 (r / 4) + r % 4 exceeds lim (one compare with a constant).
-      // A masked score becomes -inf, so P = 0 and dS = P (dP - D) = 0 exactly
-      // (dP is finite: past the sequence end K and V read as zeros). One
-      // branch around the whole tile: per-element branches would be flattened
-      // into selects that every tile pays for.
-      const int lim = (CAUSAL ? min(row, N - 1) : N - 1) - kv0 - 4 * hh;
+    // ---- LDS read offsets (elements) -----------------------------------------------
+    // With the swizzle, the operand-row read of k-step st (row 32 kb + l32, chunk
+    // 2 st + hh) sits at rw ^ 16 st (+ 32 kb D), and the transposing read of d
+    // block b (rows 16 t + 4 hh + tr_e, and + 8; column 32 b + tr_col) at
+    // tw ^ 32 b (+ 16 t D): one register each, one XOR per read.
+    int rw = tile_off<D>(l32, 8 * hh);
+    int tw0 = tile_off<D>(4 * hh + tr_e, tr_col);
+    int tw1 = tile_off<D>(4 * hh + tr_e + 8, tr_col);
+    asm volatile("" : "+v"(rw), "+v"(tw0), "+v"(tw1));
+
+    // ---- running state -----------------------------------------------------------
+    f32x16 acc[D / 32];  // dQ^T: M = d, N = this wave's 32 queries
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
+    f32x16 s[BC / 32], dp[BC / 32];  // S^T, dP^T of the tile in flight
+    u32x4 dsf[BC / 16];              // dS^T as B operands, 4 k-steps of 16 keys
+
+    // V(u): dS^T of key tile u from s, dp (= dP^T - D)
+    auto vphase = [&](int u) __attribute__((always_inline)) {
+      const int kv0 = u * BC;
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N);
+      if (need_mask) {
+        // Key kv0 + 32 kb + 8 (r / 4) + 4 hh + r % 4 is masked iff its offset
+        // 32 kb + 8 (r / 4) + r % 4 exceeds lim (one compare with a constant).
+        // A masked score becomes -inf, so P = 0 and dS = P (dP - D) = 0 exactly
+        // (dP is finite: past the sequence end K and V read as zeros). One
+        // branch around the whole tile: per-element branches would be flattened
+        // into selects that every tile pays for.
+        const int lim = (CAUSAL ? min(row, N - 1) : N - 1) - kv0 - 4 * hh;
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : s[kb][r];
+      }
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : s[kb][r];
-    }
+        for (int r = 0; r < 16; r += 2) {
+          float d2[2];
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float d2[2];
-#pragma unroll
-        for (int u2 = 0; u2 < 2; ++u2) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][r + u2], c_log2, neg_l2));
-          d2[u2] = p * dp[kb][r + u2];
+          for (int u2 = 0; u2 < 2; ++u2) {
+            const float p = fast_exp2(__builtin_fmaf(s[kb][r + u2], c_log2, neg_l2));
+            d2[u2] = p * dp[kb][r + u2];
+          }
+          dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack2<F16>(d2[0], d2[1]);
         }
-        dsf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack2<F16>(d2[0], d2[1]);
-      }
-  };
+    };
 
-  // M phase: dQ^T += K_t^T dS^T_t (if DO_DQ), then S^T, dP^T of the next tile
-  // from K_n, V_n. Operand reads run two products ahead of their use, fenced
-  // so that the scheduler keeps that depth.
-  auto mphase = [&](auto DO_DQ, const __bf16* kt, const __bf16* kn, const __bf16* vn)
-      __attribute__((always_inline)) {
-    constexpr bool do_dq = decltype(DO_DQ)::value;
-    constexpr int R = 2;
-    __builtin_amdgcn_s_setprio(1);
-    if constexpr (do_dq) {
-      constexpr int NP = (BC / 16) * (D / 32);
-      auto tread = [&](int i) {  // K^T fragment of product i: key step i / (D/32), d block i % (D/32)
-        const int t = i / (D / 32), b = i % (D / 32);
-        return cat8(ld_lds_tr(kt + (tw0 ^ (32 * b)) + 16 * t * D),
-                    ld_lds_tr(kt + (tw1 ^ (32 * b)) + 16 * t * D));
-      };
-      bf16x8 ar[R];
+    // M phase: dQ^T += K_t^T dS^T_t (if DO_DQ), then S^T, dP^T of the next tile
+    // from K_n, V_n. Operand reads run two products ahead of their use, fenced
+    // so that the scheduler keeps that depth.
+    auto mphase = [&](auto DO_DQ, const __bf16* kt, const __bf16* kn, const __bf16* vn)
+        __attribute__((always_inline)) {
+      constexpr bool do_dq = decltype(DO_DQ)::value;
+      constexpr int R = 2;
+      __builtin_amdgcn_s_setprio(1);
+      if constexpr (do_dq) {
+        constexpr int NP = (BC / 16) * (D / 32);
+        auto tread = [&](int i) {  // K^T fragment of product i: key step i / (D/32), d block i % (D/32)
+          const int t = i / (D / 32), b = i % (D / 32);
+          return cat8(ld_lds_tr(kt + (tw0 ^ (32 * b)) + 16 * t * D),
+                      ld_lds_tr(kt + (tw1 ^ (32 * b)) + 16 * t * D));
+        };
+        bf16x8 ar[R];
 #pragma unroll
-      for (int j = 0; j < R; ++j) ar[j] = tread(j);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        const int t = i / (D / 32), b = i % (D / 32);
-        acc[b] = mfma32x<F16>(ar[i % R], as_bf16x8(dsf[t]), acc[b]);
-        if (i + R < NP) ar[i % R] = tread(i + R);
+        for (int j = 0; j < R; ++j) ar[j] = tread(j);
         __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    {
-      constexpr int NP = (D / 16) * (BC / 32);
-      auto kread = [&](int i) {
-        const int st = i / (BC / 32), kb = i % (BC / 32);
-        return ld_lds16(kn + (rw ^ (16 * st)) + 32 * kb * D);
-      };
-      auto vread = [&](int i) {
-        const int st = i / (BC / 32), kb = i % (BC / 32);
-        return ld_lds16(vn + (rw ^ (16 * st)) + 32 * kb * D);
-      };
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = negd16;  // dP^T - D: every element of a lane is its query's
+        for (int i = 0; i < NP; ++i) {
+          const int t = i / (D / 32), b = i % (D / 32);
+          acc[b] = mfma32x<F16>(ar[i % R], as_bf16x8(dsf[t]), acc[b]);
+          if (i + R < NP) ar[i % R] = tread(i + R);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      bf16x8 kr[R], vr[R];
+      {
+        constexpr int NP = (D / 16) * (BC / 32);
+        auto kread = [&](int i) {
+          const int st = i / (BC / 32), kb = i % (BC / 32);
+          return ld_lds16(kn + (rw ^ (16 * st)) + 32 * kb * D);
+        };
+        auto vread = [&](int i) {
+          const int st = i / (BC / 32), kb = i % (BC / 32);
+          return ld_lds16(vn + (rw ^ (16 * st)) + 32 * kb * D);
+        };
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
-        kr[j] = kread(j);
-        vr[j] = vread(j);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int kb = 0; kb < BC / 32; ++kb) {
+          s[kb] = f32x16{};
+          dp[kb] = negd16;  // dP^T - D: every element of a lane is its query's
+        }
+        bf16x8 kr[R], vr[R];
 #pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        const int st = i / (BC / 32), kb = i % (BC / 32);
-        s[kb] = mfma32x<F16>(kr[i % R], qf[st], s[kb]);
-        if (i + R < NP) kr[i % R] = kread(i + R);
-        dp[kb] = mfma32x<F16>(vr[i % R], of[st], dp[kb]);
-        if (i + R < NP) vr[i % R] = vread(i + R);
+        for (int j = 0; j < R; ++j) {
+          kr[j] = kread(j);
+          vr[j] = vread(j);
+        }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int st = i / (BC / 32), kb = i % (BC / 32);
+          s[kb] = mfma32x<F16>(kr[i % R], qf[st], s[kb]);
+          if (i + R < NP) kr[i % R] = kread(i + R);
+          dp[kb] = mfma32x<F16>(vr[i % R], of[st], dp[kb]);
+          if (i + R < NP) vr[i % R] = vread(i + R);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-  using yes = std::true_type;
-  using no = std::false_type;
+      __builtin_amdgcn_s_setprio(0);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
 
-  // Workgroup barrier without a memory fence (tile loads are waited for
-  // explicitly; the LDS reads of a phase are consumed by its own products);
-  // the fences keep every instruction on its side.
-  auto slot_barrier = [] {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
+    // Workgroup barrier without a memory fence (tile loads are waited for
+    // explicitly; the LDS reads of a phase are consumed by its own products);
+    // the fences keep every instruction on its side.
+    auto slot_barrier = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  // ---- schedule (as in the forward kernel) ---------------------------------------
-  // Group A: S_0/dP_0 in slot 0, V(t) in slot 2t+1, M(t) in slot 2t+2; group B
-  // one slot later. K_0, K_1, V_0, V_1 are loaded up front; group B issues
-  // K_{t+2} (into the buffer of K_{t-2}, last read in slot 2t-1) and V_{t+2}
-  // (into that of V_t, last read in slot 2t+1) at the start of its V(t), slot
-  // 2t+2, and waits for them at the end of its M(t), slot 2t+3; the first
-  // reader is group A's M(t+1) in slot 2t+4.
-  // Every wave runs T4 = T rounded up to 4 tiles (the barriers must match):
-  // the full work, in groups of 4, up to its last needed tile rounded up to 4
-  // (the extra tiles are fully masked, so they add nothing), then only the
-  // loads and barriers. All T4 tiles are loaded, so no product ever reads a
-  // buffer that was never filled: a tile past the sequence end gets an empty
-  // resource (rows_rsrc) and fills its buffer with zeros without reading memory.
-  const int T4 = (T + 3) & ~3;
-  const int jw4 = (jw_last + 4) & ~3;
-  __syncthreads();  // a previous tile's epilogue may still read its dQ stage in these buffers
-  load_tile(eight{}, Kh, wave, 0, ks0);
-  load_tile(eight{}, Vh, wave, 0, vs0);
-  load_tile(eight{}, Kh, wave, 1, ks1);
-  load_tile(eight{}, Vh, wave, 1, vs1);
-  wait_vmem_all();
-  __syncthreads();
-  if (grp == 1) __syncthreads();
-  mphase(no{}, ks0, ks0, vs0);  // S_0, dP_0
-  slot_barrier();
-  // one tile t; P = t & 3 (static in each copy) names the buffers
-  auto tile = [&](auto P, int t) __attribute__((always_inline)) {
-    constexpr int p = decltype(P)::value;
-    __bf16* const kbuf[4] = {ks0, ks1, ks2, ks3};
-    __bf16* const vbuf[2] = {vs0, vs1};
-    if (grp == 1 && t + 2 < T4) {
-      load_tile(four{}, Kh, wl, t + 2, kbuf[(p + 2) & 3]);
-      load_tile(four{}, Vh, wl, t + 2, vbuf[p & 1]);
-    }
-    vphase(t);
-    slot_barrier();
-    mphase(yes{}, kbuf[p], kbuf[(p + 1) & 3], vbuf[(p + 1) & 1]);
-    wait_vmem_all();  // (group A has none in flight)
-    slot_barrier();
-  };
-  using c0 = std::integral_constant<int, 0>;
-  using c1 = std::integral_constant<int, 1>;
-  using c2 = std::integral_constant<int, 2>;
-  using c3 = std::integral_constant<int, 3>;
-  int t = 0;
-  for (; t < jw4; t += 4) {
-    tile(c0{}, t);
-    tile(c1{}, t + 1);
-    tile(c2{}, t + 2);
-    tile(c3{}, t + 3);
-  }
-  for (; t < T4; ++t) {
-    if (grp == 1 && t + 2 < T4) {
-      __bf16* kf = ((t + 2) & 3) == 0 ? ks0 : ((t + 2) & 3) == 1 ? ks1 : ((t + 2) & 3) == 2 ? ks2 : ks3;
-      load_tile(four{}, Kh, wl, t + 2, kf);
-      load_tile(four{}, Vh, wl, t + 2, (t & 1) ? vs1 : vs0);
-    }
-    slot_barrier();
+    // ---- schedule (as in the forward kernel) ---------------------------------------
+    // Group A: S_0/dP_0 in slot 0, V(t) in slot 2t+1, M(t) in slot 2t+2; group B
+    // one slot later. K_0, K_1, V_0, V_1 are loaded up front; group B issues
+    // K_{t+2} (into the buffer of K_{t-2}, last read in slot 2t-1) and V_{t+2}
+    // (into that of V_t, last read in slot 2t+1) at the start of its V(t), slot
+    // 2t+2, and waits for them at the end of its M(t), slot 2t+3; the first
+    // reader is group A's M(t+1) in slot 2t+4.
+    // Every wave runs T4 = T rounded up to 4 tiles (the barriers must match):
+    // the full work, in groups of 4, up to its last needed tile rounded up to 4
+    // (the extra tiles are fully masked, so they add nothing), then only the
+    // loads and barriers. All T4 tiles are loaded, so no product ever reads a
+    // buffer that was never filled: a tile past the sequence end gets an empty
+    // resource (rows_rsrc) and fills its buffer with zeros without reading memory.
+    const int T4 = (T + 3) & ~3;
+    const int jw4 = (jw_last + 4) & ~3;
+    __syncthreads();  // a previous tile's epilogue may still read its dQ stage in these buffers
+    load_tile(eight{}, Kh, wave, 0, ks0);
+    load_tile(eight{}, Vh, wave, 0, vs0);
+    load_tile(eight{}, Kh, wave, 1, ks1);
+    load_tile(eight{}, Vh, wave, 1, vs1);
     wait_vmem_all();
+    __syncthreads();
+    if (grp == 1) __syncthreads();
+    mphase(no{}, ks0, ks0, vs0);  // S_0, dP_0
     slot_barrier();
-  }
-  if (grp == 0) slot_barrier();
+    // one tile t; P = t & 3 (static in each copy) names the buffers
+    auto tile = [&](auto P, int t) __attribute__((always_inline)) {
+      constexpr int p = decltype(P)::value;
+      __bf16* const kbuf[4] = {ks0, ks1, ks2, ks3};
+      __bf16* const vbuf[2] = {vs0, vs1};
+      if (grp == 1 && t + 2 < T4) {
+        load_tile(four{}, Kh, wl, t + 2, kbuf[(p + 2) & 3]);
+        load_tile(four{}, Vh, wl, t + 2, vbuf[p & 1]);
+      }
+      vphase(t);
+      slot_barrier();
+      mphase(yes{}, kbuf[p], kbuf[(p + 1) & 3], vbuf[(p + 1) & 1]);
+      wait_vmem_all();  // (group A has none in flight)
+      slot_barrier();
+    };
+    using c0 = std::integral_constant<int, 0>;
+    using c1 = std::integral_constant<int, 1>;
+    using c2 = std::integral_constant<int, 2>;
+    using c3 = std::integral_constant<int, 3>;
+    int t = 0;
+    for (; t < jw4; t += 4) {
+      tile(c0{}, t);
+      tile(c1{}, t + 1);
+      tile(c2{}, t + 2);
+      tile(c3{}, t + 3);
+    }
+    for (; t < T4; ++t) {
+      if (grp == 1 && t + 2 < T4) {
+        __bf16* kf = ((t + 2) & 3) == 0 ? ks0 : ((t + 2) & 3) == 1 ? ks1 : ((t + 2) & 3) == 2 ? ks2 : ks3;
+        load_tile(four{}, Kh, wl, t + 2, kf);
+        load_tile(four{}, Vh, wl, t + 2, (t & 1) ? vs1 : vs0);
+      }
+      slot_barrier();
+      wait_vmem_all();
+      slot_barrier();
+    }
+    if (grp == 0) slot_barrier();
 
-  // ---- epilogue: dQ = scale * dQ^T, bf16, through an 8 KB LDS stage per wave
-  // in the (now idle) K tile buffers; the next tile's loads wait for a barrier
-  if (!wave_active) return;
-  __bf16* const stage = (wave < 2 ? ks0 : wave < 4 ? ks1 : wave < 6 ? ks2 : ks3) + (wave & 1) * 32 * D;
-  store_rows_via_lds<D, F16>(acc, scale, stage, dQ + head, wrow0, N);
+    // ---- epilogue: dQ = scale * dQ^T, bf16, through an 8 KB LDS stage per wave
+    // in the (now idle) K tile buffers; the next tile's loads wait for a barrier
+    if (!wave_active) return;
+    __bf16* const stage = (wave < 2 ? ks0 : wave < 4 ? ks1 : wave < 6 ? ks2 : ks3) + (wave & 1) * 32 * D;
+    store_rows_via_lds<D, F16>(acc, scale, stage, dQ + head, wrow0, N);
   };
   if constexpr (CAUSAL) {
     for (int it = 0; it < nit; ++it) run_item(it == 0 ? qt_first : wq);

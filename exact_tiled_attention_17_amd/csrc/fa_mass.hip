@@ -90,87 +90,87 @@ void key_mass_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // one key block: its sweep over the query steps and its column sums
   auto run_item = [&](const int kb) __attribute__((always_inline)) {
-  const int k0 = kb * C::BCB;
-  const int kw0 = k0 + 32 * wave;  // this wave's first key
-  const int key = kw0 + l32;       // this lane's key (column of S); rows past N read as 0
+    const int k0 = kb * C::BCB;
+    const int kw0 = k0 + 32 * wave;  // this wave's first key
+    const int key = kw0 + l32;       // this lane's key (column of S); rows past N read as 0
 
-  bf16x8 frag[D / 16];  // the lane's K row as B operands
+    bf16x8 frag[D / 16];  // the lane's K row as B operands
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    frag[s] = as_bf16x8(buf_load16(rK, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
+    for (int s = 0; s < D / 16; ++s)
+      frag[s] = as_bf16x8(buf_load16(rK, (uint32_t)key * (D * 2) + (16 * s + 8 * hh) * 2));
 
-  const int i0 = CAUSAL ? k0 / BRB : 0;  // first query tile that sees the block's keys
-  const int nsteps = nqt - i0;
-  auto load_step = [&](int s, __bf16* qd, float* ld) __attribute__((always_inline)) {
-    const int q0 = (i0 + s) * BRB;
-    const auto rQ = rows_rsrc(Qh, q0, N, D * 2);
+    const int i0 = CAUSAL ? k0 / BRB : 0;  // first query tile that sees the block's keys
+    const int nsteps = nqt - i0;
+    auto load_step = [&](int s, __bf16* qd, float* ld) __attribute__((always_inline)) {
+      const int q0 = (i0 + s) * BRB;
+      const auto rQ = rows_rsrc(Qh, q0, N, D * 2);
 #pragma unroll
-    for (int m = 0; m < LM; ++m) buf_load16_lds(rQ, src_w[m], qd + 64 * (wave + C::NW * m) * 8);
-    if (wave == 0) buf_load4_lds(rows_rsrc(Lh, q0, N, 4), 4u * lane, ld);
-  };
+      for (int m = 0; m < LM; ++m) buf_load16_lds(rQ, src_w[m], qd + 64 * (wave + C::NW * m) * 8);
+      if (wave == 0) buf_load4_lds(rows_rsrc(Lh, q0, N, 4), 4u * lane, ld);
+    };
 
-  float colsum = 0.f;  // this lane's share of its key's mass (half the rows of each block)
-  auto step = [&](int s, const __bf16* tile, const float* lse) __attribute__((always_inline)) {
-    // S for 64 queries x this wave's 32 keys: lane = one key, 16 queries per block
-    f32x16 sd[QB];
-    constexpr int NP = (D / 16) * QB;  // product i: k-step i / QB, query block i % QB
-    constexpr int R = 2;
-    auto rd = [&](int i) { return ld_lds16(tile + (rw ^ (16 * (i / QB))) + 32 * (i % QB) * D); };
+    float colsum = 0.f;  // this lane's share of its key's mass (half the rows of each block)
+    auto step = [&](int s, const __bf16* tile, const float* lse) __attribute__((always_inline)) {
+      // S for 64 queries x this wave's 32 keys: lane = one key, 16 queries per block
+      f32x16 sd[QB];
+      constexpr int NP = (D / 16) * QB;  // product i: k-step i / QB, query block i % QB
+      constexpr int R = 2;
+      auto rd = [&](int i) { return ld_lds16(tile + (rw ^ (16 * (i / QB))) + 32 * (i % QB) * D); };
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
-    bf16x8 ar[R];
+      for (int qb = 0; qb < QB; ++qb) sd[qb] = f32x16{};
+      bf16x8 ar[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) ar[j] = rd(j);
+      for (int j = 0; j < R; ++j) ar[j] = rd(j);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      sd[i % QB] = mfma32x<F16>(ar[i % R], frag[i / QB], sd[i % QB]);
-      if (i + R < NP) ar[i % R] = rd(i + R);
-    }
-    // P = exp2(c S - LSE2), masked: query q0 + m (m = 32 qb + 8 g + 4 hh + e)
-    // counts iff (unsigned)(m + mbase) < mbound (it exists and, if causal,
-    // is at or after the key); a key past the end collects nothing
-    const int q0 = (i0 + s) * BRB;
-    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + BRB > N);
-    const int qlo = CAUSAL ? key : 0;
-    const int mbase = q0 - qlo;
-    const unsigned mbound = key < N ? (unsigned)(N - qlo) : 0u;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m0 = 32 * qb + 8 * g + 4 * hh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse[m0]);
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p[e] = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l4[e] * kLog2e));
-        if (need_mask) {  // selects under one wave-uniform branch
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = (unsigned)(m0 + e + mbase) >= mbound ? 0.f : p[e];
-        }
-        colsum += (p[0] + p[1]) + (p[2] + p[3]);
+      for (int i = 0; i < NP; ++i) {
+        sd[i % QB] = mfma32x<F16>(ar[i % R], frag[i / QB], sd[i % QB]);
+        if (i + R < NP) ar[i % R] = rd(i + R);
       }
-  };
-  barrier();  // the previous block's last step is read by every wave
-  load_step(0, qs0, ls0);
-  wait_vmem_all();
-  barrier();
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    load_step(s + 1, qs1, ls1);
-    step(s, qs0, ls0);
-    wait_vmem_all();  // step s + 1 has landed (every wave, after the barrier)
-    barrier();        // ... and nobody reads buffer 0 any more
-    if (s + 2 < nsteps) load_step(s + 2, qs0, ls0);
-    step(s + 1, qs1, ls1);
+      // P = exp2(c S - LSE2), masked: query q0 + m (m = 32 qb + 8 g + 4 hh + e)
+      // counts iff (unsigned)(m + mbase) < mbound (it exists and, if causal,
+      // is at or after the key); a key past the end collects nothing
+      const int q0 = (i0 + s) * BRB;
+      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + BRB > N);
+      const int qlo = CAUSAL ? key : 0;
+      const int mbase = q0 - qlo;
+      const unsigned mbound = key < N ? (unsigned)(N - qlo) : 0u;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m0 = 32 * qb + 8 * g + 4 * hh;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse[m0]);
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[e] = fast_exp2(__builtin_fmaf(sd[qb][4 * g + e], c_log2, -l4[e] * kLog2e));
+          if (need_mask) {  // selects under one wave-uniform branch
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = (unsigned)(m0 + e + mbase) >= mbound ? 0.f : p[e];
+          }
+          colsum += (p[0] + p[1]) + (p[2] + p[3]);
+        }
+    };
+    barrier();  // the previous block's last step is read by every wave
+    load_step(0, qs0, ls0);
     wait_vmem_all();
     barrier();
-  }
-  if (s < nsteps) step(s, qs0, ls0);
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      load_step(s + 1, qs1, ls1);
+      step(s, qs0, ls0);
+      wait_vmem_all();  // step s + 1 has landed (every wave, after the barrier)
+      barrier();        // ... and nobody reads buffer 0 any more
+      if (s + 2 < nsteps) load_step(s + 2, qs0, ls0);
+      step(s + 1, qs1, ls1);
+      wait_vmem_all();
+      barrier();
+    }
+    if (s < nsteps) step(s, qs0, ls0);
 
-  // the two half-waves hold the other rows of the same keys
-  colsum += __shfl_xor(colsum, 32);
-  if (hh == 0 && key < N) part[(size_t)bh * N + key] = colsum;
+    // the two half-waves hold the other rows of the same keys
+    colsum += __shfl_xor(colsum, 32);
+    if (hh == 0 && key < N) part[(size_t)bh * N + key] = colsum;
   };
   if constexpr (CAUSAL) {
     for (int it = 0; it < nit; ++it) run_item(it == 0 ? wb : nkb - 1 - wb);
