@@ -21,7 +21,10 @@
 //                                       accumulator starts at -D)
 //        P = exp2(c S - LSE2), dS = P (dP - D)
 //        dV += P^T dO, dK += dS^T Q    (P^T, dS^T straight from registers)
-//     Causal: query tiles that see none of the block's keys are skipped.
+//     Causal: query tiles that see none of the block's keys are skipped, and
+//     a workgroup takes key blocks kb and nkb - 1 - kb in turn (equal work per
+//     workgroup), its step pipeline running from one block into the other.
+//     The dQ pass likewise pairs query tiles nq - 1 - w and w.
 //  (3. bwd_reduce_kernel, only when the dK/dV work of few K/V heads is split
 //     over several workgroups: sums their float32 partials.)
 //

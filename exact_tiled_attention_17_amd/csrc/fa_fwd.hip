@@ -27,7 +27,12 @@
 //    the other runs its softmax. Each phase ends at a workgroup barrier.
 //  * Causal: tiles entirely above the diagonal are never loaded; a wave skips
 //    the work of tiles fully masked for its own rows; masks are applied only to
-//    tiles that cross the diagonal or the end of the sequence.
+//    tiles that cross the diagonal or the end of the sequence. A workgroup
+//    runs two query tiles, nq - 1 - w and then w, so that all workgroups do
+//    the same number of key tiles (uneven workgroups leave CUs idle while
+//    work is still queued).
+//  * O leaves through LDS: each wave writes its finished rows into a stage in
+//    the idle K/V buffers and stores them as whole rows.
 //  * The softmax runs in base 2 in float32: c = scale * log2(e) is folded into
 //    one FMA per score; P is rounded to bf16 for the matrix core. The row sum
 //    l is a product too: an all-ones A operand against the same P^T operands
