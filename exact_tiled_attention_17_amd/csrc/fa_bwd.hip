@@ -653,20 +653,32 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const int r = p / CH, pc = p % CH;
       return (uint32_t)(r * (D * 2) + ((pc ^ swz<D>(r)) * 16));
     };
-    constexpr int LM = (TI + 3) / 4;
-    uint32_t src_b[LM];  // this wave's offsets as one of the four in-loop loaders
-#pragma unroll
-    for (int m = 0; m < LM; ++m) src_b[m] = src(wl + 4 * m);
+    // This wave's offsets as one of the four in-loop loaders: instructions
+    // wl + 4 m lie 256 chunks (4096 bytes, 256 / CH rows, a whole number of
+    // swizzle periods) apart. The first is formed at each tile load from a
+    // fresh lane index (v_mbcnt), so that no register is held for them
+    // across the tile loop (the compiler spilled them, and reloaded and
+    // waited for them at every tile).
+    static_assert((256 / CH) % 16 == 0, "in-loop loader offsets step by whole swizzle periods");
     // tile j of K or V (src = the head's first row), through a resource that
     // starts at the tile's first key and ends at key N
     auto load_tile = [&](auto NL, const __bf16* src_head, int w, int j, __bf16* t)
         __attribute__((always_inline)) {
       constexpr int nl = decltype(NL)::value;
       const auto r = rows_rsrc(src_head, j * BC, N, D * 2);
+      uint32_t o0 = 0;
+      if constexpr (nl == 4) {
+        uint32_t ln;  // the lane index, formed here (volatile: not merged with the kernel's own)
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const uint32_t p = 64u * (uint32_t)w + ln;
+        const int rr = (int)(p / CH), pc = (int)(p % CH);
+        o0 = (uint32_t)(rr * (D * 2) + ((pc ^ swz<D>(rr)) * 16));
+        asm volatile("" : "+v"(o0));
+      }
 #pragma unroll
       for (int m = 0; m * nl < TI; ++m) {
         const int n = m * nl + w;
-        if (n < TI) buf_load16_lds(r, nl == 4 ? src_b[m] : src(n), t + 64 * n * 8);
+        if (n < TI) buf_load16_lds(r, nl == 4 ? o0 + 4096u * m : src(n), t + 64 * n * 8);
       }
     };
     using four = std::integral_constant<int, 4>;
