@@ -7,7 +7,10 @@
 // MI355X:
 //
 //  * One workgroup owns BR = 32 * NW query rows of one (batch, head); each of
-//    its NW waves owns 32 of them for the whole sweep over the keys.
+//    its NW waves owns 32 of them for the whole sweep over the keys. The
+//    query tile is staged in LDS (loaded with the first K/V tiles, 1 KB of
+//    consecutive bytes per instruction); each wave then keeps its rows in
+//    registers, as the B operand of S^T = K Q^T, for the whole sweep.
 //  * Both products are computed transposed, S^T = K Q^T and O^T = V^T P^T,
 //    on 32x32x16 bf16 matrix cores. In the accumulator layout of S^T every lane
 //    then holds 16 scores of a single query row (its partner lane l ^ 32 holds
@@ -129,6 +132,9 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // use the first BC * (D + 16) bytes of ks0 / ks1
   __shared__ __attribute__((aligned(16))) uint32_t ksc0[QM == 2 ? BC : 1];
   __shared__ __attribute__((aligned(16))) uint32_t ksc1[QM == 2 ? BC : 1];
+  // bf16/f16 path: the query tile's rows, loaded straight into LDS with the
+  // tile loads; row r's 16-byte chunk c at c ^ (r mod CH)
+  __shared__ __attribute__((aligned(16))) __bf16 qst[QM == 0 ? BR * D : 8];
 
   // With `pairs` (causal only) the workgroup runs query tile nq - 1 - w and
   // then tile w: every pair has the same number of key tiles, so the
@@ -176,9 +182,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // last key tile this wave needs (-1: none)
     const int jw_last = !wave_active ? -1 : CAUSAL ? min(wrow0 + 31, N - 1) / BC : T - 1;
 
-    // ---- Q^T operand: lane holds row `row`, d = 16 s + 8 hh .. +7 (0 past N) --
+    // ---- Q^T operand: lane holds row `row`, d = 16 s + 8 hh .. +7 (0 past N).
+    // QM 0 stages the query tile in LDS first (in the prologue below, with the
+    // K/V tiles); QM 1 loads it here, as its in-register quantisation needs.
     bf16x8 qf[QM == 2 ? 1 : D / 16];
-    if constexpr (QM != 2) {
+    if constexpr (QM == 1) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
         qf[s] = as_bf16x8(buf_load16(rQ, (uint32_t)row * (D * 2) + (16 * s + 8 * hh) * 2));
@@ -515,11 +523,28 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // and waits for them at the end of its M(t), slot 2t+3; their first reader is
     // group A's M(t+1) in slot 2t+4.
     __syncthreads();  // a previous tile's epilogue may still read its O stage in these buffers
+    if constexpr (QM == 0) {
+      // the query tile into the stage: instruction n = wave + 8 m fills rows
+      // RPI n .. RPI n + RPI - 1 (whole rows, 1 KB of consecutive bytes); the
+      // rows of m and m + 1 lie 8 RPI (a multiple of CH) apart, so the
+      // swizzle and the offsets within them repeat, 8192 bytes further on
+      constexpr int RPI = 64 / CH, QI = BR * D * 2 / 1024 / 8;
+      const auto r = rows_rsrc(Q + head, q0, N, D * 2);
+      const int rl = RPI * wave + lane / CH, sl = lane % CH;
+      const uint32_t base = (uint32_t)(rl * (D * 2) + ((sl ^ (rl & (CH - 1))) * 16));
+#pragma unroll
+      for (int m = 0; m < QI; ++m) buf_load16_lds(r, base + 8192u * m, qst + 64 * (wave + 8 * m) * 8);
+    }
     load_k(eight{}, wave, 0, ks0, ksc0);
     if (T > 1) load_k(eight{}, wave, 1, ks1, ksc1);
     load_v(eight{}, wave, 0, vs0);
     wait_vmem_all();
     __syncthreads();
+    if constexpr (QM == 0) {
+      const __bf16* const qrow = qst + (32 * rblk + l32) * D;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[s] = ld_lds16(qrow + 8 * ((2 * s + hh) ^ (l32 & (CH - 1))));
+    }
     if (grp == 1) __syncthreads();
     mphase(yes{}, no{}, ks0, vs0, ksc0);  // S_0
     slot_barrier();
