@@ -77,7 +77,8 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to IEEE binary16 (numpy's conversion: round to
     nearest, ties to even; overflow to infinity) and return the uint16 bits."""
-    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):  # the overflow to infinity is the intended result
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
 def normal_bf16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:

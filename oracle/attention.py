@@ -45,7 +45,9 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     the high 16 bits of a uint32 gives the float32 with the same value.
     """
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return u.view(np.float32).astype(np.float64)
+    # signalling-NaN patterns raise the invalid flag when widened; they stay NaN
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
 
 
 def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
